@@ -1,0 +1,349 @@
+"""Pins of the CPU oracle: checks against facts fixed outside the oracle itself.
+
+Each ``pin_*`` function raises ``AssertionError`` when the oracle disagrees
+with a closed form, a brute-force or library computation, an invariant, or a
+worked example printed on the pages.  ``test_oracle.py`` runs them as tests;
+``test_oracle_mutations.py`` plants plausible mistakes in the oracle and
+checks that some pin catches each one.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+import oracle
+from workloads import (BF16_NAN, bf16_bits_from_f32, config, cu_seqlens_from_lens, decode_case,
+                       prefill_case, slot_for_position)
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+SCALE64 = np.float32(0.125)  # 1/sqrt(64), exact
+
+
+def _bits(values) -> np.ndarray:
+    return bf16_bits_from_f32(np.asarray(values, dtype=np.float32))
+
+
+def _pool_from_logical(logical, table, block_size, num_blocks):
+    """Page logical rows into a NaN-filled pool one token at a time (test-side construction)."""
+    Hkv, D = logical.shape[1], logical.shape[2]
+    pool = np.full((num_blocks, block_size, Hkv, D), BF16_NAN, dtype=np.uint16)
+    for j in range(logical.shape[0]):
+        pool[table[j // block_size], j % block_size] = logical[j]
+    return pool
+
+
+def _single_seq_decode(q, K, V, scale, block_size=16, seed=0):
+    """Oracle decode of one sequence given contiguous logical K/V ([n, Hkv, D] bits)."""
+    n = K.shape[0]
+    nblk = -(-n // block_size)
+    rng = np.random.default_rng(seed)
+    table = rng.permutation(nblk + 3)[:nblk].astype(np.int32)
+    kp = _pool_from_logical(K, table, block_size, nblk + 3)
+    vp = _pool_from_logical(V, table, block_size, nblk + 3)
+    return oracle.paged_decode(q[None], kp, vp, table[None], np.array([n], np.int32), scale)[0]
+
+
+# --------------------------------------------------------------------------- format / examples
+
+def pin_bf16_decode():
+    """bfloat16 is the top half of a float32: values fixed by the format."""
+    bits = np.array([0x3F80, 0xBF80, 0x4049, 0x0001, 0x7F80, 0x3F81, 0x0000, 0xC2F7], np.uint16)
+    want = [1.0, -1.0, 3.140625, 2.0 ** -133, math.inf, 1.0 + 2.0 ** -7, 0.0, -123.5]
+    got = oracle.bf16_to_f64(bits)
+    assert got.tolist() == want, got
+
+
+def pin_cu_seqlens_example():
+    g = json.load(open(os.path.join(GOLDEN, "cu_seqlens_example.json")))
+    assert cu_seqlens_from_lens(g["q_lens"]).tolist() == g["cu_seqlens_q"]
+
+
+def pin_block_boundary_example():
+    """The 257th token of a sequence with block size 256 goes to offset 0 of the second block."""
+    g = json.load(open(os.path.join(GOLDEN, "slot_block_boundary.json")))
+    bs, table = g["block_size"], g["block_table"]
+    pos = g["new_token_position"]
+    assert (g["tokens_before"] % bs == 0) and ((g["tokens_before"] + 1) % bs == 1)
+    slot = table[-1] * bs + g["last_block_num_tokens"] - 1
+    assert slot == g["expected_slot"] == slot_for_position(table, pos, bs)
+    rng = np.random.default_rng(3)
+    Hkv, D, NB = 1, 64, 6
+    pool_k = np.full((NB, bs, Hkv, D), BF16_NAN, np.uint16)
+    first = _bits(rng.standard_normal((bs, Hkv, D)))
+    pool_k[g["full_block_of_first_256"]] = first
+    new_k = _bits(rng.standard_normal((1, Hkv, D)))
+    kc, _ = oracle.kvcache_store(new_k, new_k, np.array([slot], np.int32), pool_k, pool_k.copy())
+    assert np.array_equal(kc[g["expected_block"], g["expected_offset"]], new_k[0])
+    rows = oracle.unpage(kc, np.array(table, np.int32), pos + 1)
+    assert np.array_equal(rows[:bs], first)
+    assert np.array_equal(rows[pos], new_k[0])
+
+
+# --------------------------------------------------------------------------- store and un-page
+
+def pin_store_writes_exactly_mapped_slots():
+    rng = np.random.default_rng(5)
+    NB, BS, Hkv, D, T = 9, 8, 2, 64, 20
+    base = rng.integers(0, 1 << 16, size=(NB, BS, Hkv, D), dtype=np.uint16)
+    k = rng.integers(0, 1 << 16, size=(T, Hkv, D), dtype=np.uint16)
+    v = rng.integers(0, 1 << 16, size=(T, Hkv, D), dtype=np.uint16)
+    slots = rng.choice(NB * BS, size=T, replace=False).astype(np.int32)
+    slots[[3, 11]] = -1
+    kc, vc = oracle.kvcache_store(k, v, slots, base, base.copy())
+    where = {int(s): t for t, s in enumerate(slots) if s >= 0}
+    for b in range(NB):
+        for o in range(BS):
+            t = where.get(b * BS + o)
+            exp_k = base[b, o] if t is None else k[t]
+            exp_v = base[b, o] if t is None else v[t]
+            assert np.array_equal(kc[b, o], exp_k) and np.array_equal(vc[b, o], exp_v), (b, o)
+
+
+def pin_unpage_round_trip():
+    """Paging token by token, then un-paging, gives the logical rows back bit for bit."""
+    rng = np.random.default_rng(6)
+    for BS, n in ((16, 37), (8, 8), (4, 1), (32, 95)):
+        nblk = -(-n // BS)
+        table = rng.permutation(nblk + 5)[:nblk]
+        logical = rng.integers(0, 1 << 16, size=(n, 2, 64), dtype=np.uint16)
+        pool = _pool_from_logical(logical, table, BS, nblk + 5)
+        assert np.array_equal(oracle.unpage(pool, table, n), logical)
+
+
+def pin_generator_pages_what_oracle_unpages():
+    """The workload generator's pool holds each sequence's logical rows (also shared prefixes)."""
+    c = config(1, keep_logical=True)
+    for i in range(c.batch):
+        n = int(c.context_lens[i]) - 1
+        assert np.array_equal(oracle.unpage(c.k_cache, c.block_tables[i], n), c.logical_k[i])
+        assert np.array_equal(oracle.unpage(c.v_cache, c.block_tables[i], n), c.logical_v[i])
+    s = decode_case(4, [40, 35, 50, 9], 2, 1, 64, 8, nb_factor=1.5, shared_groups=[[0, 2]],
+                    shared_blocks=[4], keep_logical=True)
+    assert s.block_tables[0, :4].tolist() == s.block_tables[2, :4].tolist()
+    for i in range(s.batch):
+        n = int(s.context_lens[i]) - 1
+        assert np.array_equal(oracle.unpage(s.k_cache, s.block_tables[i], n), s.logical_k[i])
+
+
+# --------------------------------------------------------------------------- attention values
+
+def _brute_force(q, K, V, scale):
+    """Softmax attention with Python floats and math.exp, no paging, no NumPy."""
+    qf = [float(x) for x in q]
+    scores = [sum(a * b for a, b in zip(qf, row)) * float(scale) for row in K]
+    top = max(scores)
+    w = [math.exp(s - top) for s in scores]
+    tot = sum(w)
+    return [sum(w[j] * V[j][d] for j in range(len(V))) / tot for d in range(len(V[0]))]
+
+
+def pin_decode_matches_brute_force():
+    rng = np.random.default_rng(7)
+    for ctx, Hq, Hkv in (([1, 9, 23], 2, 1), ([31, 5], 4, 2), ([17], 4, 1)):
+        c = decode_case(int(rng.integers(1 << 30)), ctx, Hq, Hkv, 64, 8, nb_factor=2.0,
+                        keep_logical=True)
+        kc, vc = oracle.kvcache_store(c.k_new, c.v_new, c.slot_mapping, c.k_cache, c.v_cache)
+        out = oracle.paged_decode(c.q, kc, vc, c.block_tables, c.context_lens, SCALE64)
+        G = Hq // Hkv
+        for i in range(c.batch):
+            K = np.concatenate([c.logical_k[i], c.k_new[i:i + 1]])
+            V = np.concatenate([c.logical_v[i], c.v_new[i:i + 1]])
+            for h in range(Hq):
+                g = h // G
+                Kg = oracle.bf16_to_f64(K[:, g]).tolist()
+                Vg = oracle.bf16_to_f64(V[:, g]).tolist()
+                ref = _brute_force(oracle.bf16_to_f64(c.q[i, h]), Kg, Vg, SCALE64)
+                assert np.max(np.abs(out[i, h] - np.array(ref))) < 1e-12, (i, h)
+
+
+def pin_decode_matches_torch_sdpa():
+    """torch's CPU scaled_dot_product_attention (float64) on the un-paged K/V."""
+    import torch.nn.functional as F
+    rng = np.random.default_rng(8)
+    for D, BS, Hq, Hkv, ctx in ((128, 16, 8, 8, [300, 1, 129]), (128, 32, 14, 2, [77, 250]),
+                                (64, 8, 8, 1, [64, 65, 3])):
+        c = decode_case(int(rng.integers(1 << 30)), ctx, Hq, Hkv, D, BS, nb_factor=1.3,
+                        keep_logical=True)
+        kc, vc = oracle.kvcache_store(c.k_new, c.v_new, c.slot_mapping, c.k_cache, c.v_cache)
+        scale = np.float32(1 / math.sqrt(D))
+        out = oracle.paged_decode(c.q, kc, vc, c.block_tables, c.context_lens, scale)
+        for i in range(c.batch):
+            K = oracle.bf16_to_f64(np.concatenate([c.logical_k[i], c.k_new[i:i + 1]]))
+            V = oracle.bf16_to_f64(np.concatenate([c.logical_v[i], c.v_new[i:i + 1]]))
+            qt = torch.from_numpy(oracle.bf16_to_f64(c.q[i]))[:, None, :]          # [Hq, 1, D]
+            Kt = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)  # [Hq, n, D]
+            Vt = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)
+            ref = F.scaled_dot_product_attention(qt, Kt.contiguous(), Vt.contiguous(),
+                                                 scale=float(scale))[:, 0, :].numpy()
+            assert np.max(np.abs(out[i] - ref)) < 1e-10, i
+
+
+def pin_one_token_context_returns_v():
+    c = decode_case(9, [1, 1, 1], 4, 2, 128, 16, nb_factor=2.0)
+    kc, vc = oracle.kvcache_store(c.k_new, c.v_new, c.slot_mapping, c.k_cache, c.v_cache)
+    out = oracle.paged_decode(c.q, kc, vc, c.block_tables, c.context_lens, np.float32(0.0883883))
+    for i in range(3):
+        for h in range(4):
+            assert np.array_equal(out[i, h], oracle.bf16_to_f64(c.v_new[i, h // 2]))
+
+
+def pin_constant_values_and_uniform_keys():
+    rng = np.random.default_rng(10)
+    n, D = 45, 64
+    q = _bits(rng.standard_normal((1, D)))
+    K = _bits(rng.standard_normal((n, 1, D)))
+    V = np.broadcast_to(_bits(rng.standard_normal(D)), (n, 1, D)).copy()
+    out = _single_seq_decode(q, K, V, SCALE64)
+    assert np.max(np.abs(out[0] - oracle.bf16_to_f64(V[0, 0]))) < 1e-14
+    K_same = np.broadcast_to(K[0], (n, 1, D)).copy()
+    V_rand = _bits(rng.standard_normal((n, 1, D)))
+    out = _single_seq_decode(q, K_same, V_rand, SCALE64)
+    assert np.max(np.abs(out[0] - oracle.bf16_to_f64(V_rand[:, 0]).mean(axis=0))) < 1e-12
+    out = _single_seq_decode(np.zeros_like(q), K, V_rand, SCALE64)
+    assert np.max(np.abs(out[0] - oracle.bf16_to_f64(V_rand[:, 0]).mean(axis=0))) < 1e-12
+
+
+def pin_two_key_closed_form():
+    """Two keys with dot products 2 and 6, scale 1/8: weights are sigmoid(-1/2) and sigmoid(1/2)."""
+    D = 64
+    q = np.zeros((1, D), np.float32); q[0, 0] = 2.0
+    K = np.zeros((2, 1, D), np.float32); K[0, 0, 0] = 1.0; K[1, 0, 0] = 3.0
+    V = np.zeros((2, 1, D), np.float32); V[0, 0, :] = 1.0; V[1, 0, :] = -1.0; V[1, 0, 5] = 4.0
+    out = _single_seq_decode(_bits(q), _bits(K), _bits(V), SCALE64)[0]
+    w1 = 1.0 / (1.0 + math.exp(-0.5))
+    want = (1 - w1) * 1.0 + w1 * (-1.0)
+    assert abs(out[0] - want) < 1e-14 and abs(out[63] - want) < 1e-14
+    assert abs(out[5] - ((1 - w1) * 1.0 + w1 * 4.0)) < 1e-14
+
+
+def pin_scale_multiplies_dot_product():
+    """scale 1/8 on q equals scale 1 on q/8 (q/8 is exact in bfloat16)."""
+    rng = np.random.default_rng(11)
+    n, D = 30, 64
+    qf = rng.standard_normal((1, D)).astype(np.float32)
+    q = _bits(qf)
+    q8 = _bits(oracle.bf16_to_f64(q).astype(np.float32) / 8)
+    K = _bits(rng.standard_normal((n, 1, D)))
+    V = _bits(rng.standard_normal((n, 1, D)))
+    a = _single_seq_decode(q, K, V, SCALE64)
+    b = _single_seq_decode(q8, K, V, np.float32(1.0))
+    assert np.max(np.abs(a - b)) < 1e-14
+
+
+def pin_gqa_head_mapping():
+    """KV head g holds V == g + 1 everywhere, so query head h must return h // G + 1."""
+    Hq, Hkv, D, BS = 8, 4, 64, 8
+    c = decode_case(13, [20, 9], Hq, Hkv, D, BS, nb_factor=2.0)
+    vc = c.v_cache.copy()
+    v_new = c.v_new.copy()
+    for g in range(Hkv):
+        val = _bits(np.float32(g + 1))
+        vc[:, :, g, :] = np.where(c.v_cache[:, :, g, :] == BF16_NAN, BF16_NAN, val)
+        v_new[:, g, :] = val
+    kc, vc = oracle.kvcache_store(c.k_new, v_new, c.slot_mapping, c.k_cache, vc)
+    out = oracle.paged_decode(c.q, kc, vc, c.block_tables, c.context_lens, SCALE64)
+    for h in range(Hq):
+        assert np.max(np.abs(out[:, h] - (h // (Hq // Hkv) + 1))) < 1e-14, h
+
+
+def pin_gqa_equals_expanded_heads():
+    """Repeating each KV head G times and running with G = 1 gives the same output."""
+    Hq, Hkv = 6, 2
+    c = decode_case(14, [33, 7, 18], Hq, Hkv, 64, 8, nb_factor=1.5)
+    kc, vc = oracle.kvcache_store(c.k_new, c.v_new, c.slot_mapping, c.k_cache, c.v_cache)
+    a = oracle.paged_decode(c.q, kc, vc, c.block_tables, c.context_lens, SCALE64)
+    G = Hq // Hkv
+    b = oracle.paged_decode(c.q, np.repeat(kc, G, axis=2), np.repeat(vc, G, axis=2),
+                            c.block_tables, c.context_lens, SCALE64)
+    assert np.array_equal(a, b)
+
+
+def pin_block_permutation_invariance():
+    c = decode_case(15, [50, 17, 64, 3], 4, 2, 64, 16, nb_factor=1.7)
+    kc, vc = oracle.kvcache_store(c.k_new, c.v_new, c.slot_mapping, c.k_cache, c.v_cache)
+    a = oracle.paged_decode(c.q, kc, vc, c.block_tables, c.context_lens, SCALE64)
+    perm = np.random.default_rng(16).permutation(c.num_blocks)
+    kp, vp = np.empty_like(kc), np.empty_like(vc)
+    kp[perm] = kc
+    vp[perm] = vc
+    bt = np.where(c.block_tables >= 0, perm[np.maximum(c.block_tables, 0)], -1).astype(np.int32)
+    b = oracle.paged_decode(c.q, kp, vp, bt, c.context_lens, SCALE64)
+    assert np.array_equal(a, b)
+
+
+def pin_padded_row_is_zero_and_unused_slots_unread():
+    c = decode_case(17, [0, 20, 0, 5], 2, 1, 64, 8, nb_factor=1.5)
+    kc, vc = oracle.kvcache_store(c.k_new, c.v_new, c.slot_mapping, c.k_cache, c.v_cache)
+    out = oracle.paged_decode(c.q, kc, vc, c.block_tables, c.context_lens, SCALE64)
+    assert np.all(out[0] == 0) and np.all(out[2] == 0)
+    assert np.all(np.isfinite(out))  # the pool's unused slots are NaN
+
+
+# --------------------------------------------------------------------------- prefill
+
+def _prefill_inputs(seed, P, n, Hq=4, Hkv=2, D=64, BS=8):
+    return prefill_case(seed, P, n, Hq, Hkv, D, BS, keep_logical=True)
+
+
+def pin_prefill_rows_equal_decode_steps():
+    """Chunk row t equals a decode of that token over the first P + t + 1 tokens."""
+    p = _prefill_inputs(18, [0, 13, 24], [6, 9, 1])
+    out = oracle.paged_prefill(p.q, p.k_new, p.v_new, p.cu_seqlens_q, p.k_cache, p.v_cache,
+                               p.block_tables, p.context_lens, SCALE64)
+    kc, vc = oracle.kvcache_store(p.k_new, p.v_new, p.slot_mapping, p.k_cache, p.v_cache)
+    for i in range(p.batch):
+        for t in range(int(p.q_lens[i])):
+            row = int(p.cu_seqlens_q[i]) + t
+            ctx = np.array([int(p.prefix_lens[i]) + t + 1], np.int32)
+            dec = oracle.paged_decode(p.q[row:row + 1], kc, vc, p.block_tables[i:i + 1], ctx,
+                                      SCALE64)
+            assert np.max(np.abs(out[row] - dec[0])) < 1e-12, (i, t)
+
+
+def pin_prefill_first_token_without_prefix_is_its_v():
+    p = _prefill_inputs(19, [0, 0], [3, 5])
+    out = oracle.paged_prefill(p.q, p.k_new, p.v_new, p.cu_seqlens_q, p.k_cache, p.v_cache,
+                               p.block_tables, p.context_lens, SCALE64)
+    for i in range(2):
+        row = int(p.cu_seqlens_q[i])
+        for h in range(4):
+            assert np.array_equal(out[row, h], oracle.bf16_to_f64(p.v_new[row, h // 2]))
+
+
+def pin_prefill_matches_torch_sdpa_with_mask():
+    import torch.nn.functional as F
+    p = _prefill_inputs(20, [11, 0, 40], [7, 12, 16], Hq=6, Hkv=3, D=64, BS=16)
+    out = oracle.paged_prefill(p.q, p.k_new, p.v_new, p.cu_seqlens_q, p.k_cache, p.v_cache,
+                               p.block_tables, p.context_lens, SCALE64)
+    for i in range(p.batch):
+        a, b = int(p.cu_seqlens_q[i]), int(p.cu_seqlens_q[i + 1])
+        P, n = int(p.prefix_lens[i]), b - a
+        K = oracle.bf16_to_f64(np.concatenate([p.logical_k[i], p.k_new[a:b]]))
+        V = oracle.bf16_to_f64(np.concatenate([p.logical_v[i], p.v_new[a:b]]))
+        mask = torch.ones(n, P + n, dtype=torch.bool).tril(diagonal=P)  # bottom-right aligned
+        qt = torch.from_numpy(oracle.bf16_to_f64(p.q[a:b])).permute(1, 0, 2)
+        Kt = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(2, 0).contiguous()
+        Vt = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(2, 0).contiguous()
+        ref = F.scaled_dot_product_attention(qt, Kt, Vt, attn_mask=mask, scale=0.125)
+        assert np.max(np.abs(out[a:b] - ref.permute(1, 0, 2).numpy())) < 1e-10, i
+
+
+def pin_prefill_is_causal():
+    """Changing the K/V of later chunk tokens leaves earlier rows bit-identical."""
+    p = _prefill_inputs(21, [9], [10])
+    out = oracle.paged_prefill(p.q, p.k_new, p.v_new, p.cu_seqlens_q, p.k_cache, p.v_cache,
+                               p.block_tables, p.context_lens, SCALE64)
+    k2, v2 = p.k_new.copy(), p.v_new.copy()
+    k2[6:] ^= 0x1234
+    v2[6:] ^= 0x0F0F
+    out2 = oracle.paged_prefill(p.q, k2, v2, p.cu_seqlens_q, p.k_cache, p.v_cache,
+                                p.block_tables, p.context_lens, SCALE64)
+    assert np.array_equal(out[:6], out2[:6])
+    assert not np.array_equal(out[6:], out2[6:])
+
+
+PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

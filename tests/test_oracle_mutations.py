@@ -1,0 +1,98 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins catch each one."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.paged_attention as pa_oracle
+from oracle_pins import PINS
+
+
+def _caught(monkeypatch, name, replacement):
+    monkeypatch.setattr(pa_oracle, name, replacement)
+    if hasattr(oracle, name):
+        monkeypatch.setattr(oracle, name, replacement)
+    failed = []
+    for pin in PINS:
+        try:
+            pin()
+        except (AssertionError, IndexError, ValueError, FloatingPointError):
+            failed.append(pin.__name__)
+    return failed
+
+
+def _softmax_no_scale(q_rows, K, V, scale, mask=None):
+    s = q_rows @ K.T
+    if mask is not None:
+        s = np.where(mask, s, -np.inf)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    return (p @ V) / p.sum(axis=1, keepdims=True)
+
+
+def _softmax_sign(q_rows, K, V, scale, mask=None):
+    s = -(q_rows @ K.T) * float(scale)
+    if mask is not None:
+        s = np.where(mask, s, -np.inf)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    return (p @ V) / p.sum(axis=1, keepdims=True)
+
+
+def _softmax_values_are_keys(q_rows, K, V, scale, mask=None):
+    s = (q_rows @ K.T) * float(scale)
+    if mask is not None:
+        s = np.where(mask, s, -np.inf)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    return (p @ K) / p.sum(axis=1, keepdims=True)
+
+
+def _softmax_unnormalised(q_rows, K, V, scale, mask=None):
+    s = (q_rows @ K.T) * float(scale)
+    if mask is not None:
+        s = np.where(mask, s, -np.inf)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    return p @ V
+
+
+def _unpage_swapped(cache, table_row, n):
+    bs = cache.shape[1]
+    j = np.arange(int(n))
+    return cache[np.asarray(table_row, np.int64)[j % len(table_row) if len(table_row) else j],
+                 (j // max(len(table_row), 1)) % bs]
+
+
+def _unpage_offset_by_one(cache, table_row, n):
+    bs = cache.shape[1]
+    j = np.arange(int(n)) + 1
+    return cache[np.asarray(table_row, np.int64)[np.minimum(j // bs, len(table_row) - 1)], j % bs]
+
+
+def _store_next_slot(k, v, slot_mapping, k_cache, v_cache):
+    shifted = np.where(np.asarray(slot_mapping) >= 0, np.asarray(slot_mapping) + 1, -1)
+    shifted = np.minimum(shifted, k_cache.shape[0] * k_cache.shape[1] - 1)
+    return ORIGINAL_STORE(k, v, shifted, k_cache, v_cache)
+
+
+ORIGINAL_STORE = pa_oracle.kvcache_store
+
+MUTATIONS = {
+    "gqa_modulo": ("kv_head_for", lambda h, g: h % max(1, g) if g > 1 else h // g),
+    "causal_excludes_self": ("visible", lambda t, j, P: j < P + t),
+    "causal_ignores_prefix": ("visible", lambda t, j, P: j <= t + 0 * P),
+    "no_mask": ("visible", lambda t, j, P: (j >= 0) | (t >= 0)),
+    "scale_dropped": ("softmax_attention", _softmax_no_scale),
+    "score_sign": ("softmax_attention", _softmax_sign),
+    "values_are_keys": ("softmax_attention", _softmax_values_are_keys),
+    "not_normalised": ("softmax_attention", _softmax_unnormalised),
+    "unpage_swapped_axes": ("unpage", _unpage_swapped),
+    "unpage_off_by_one": ("unpage", _unpage_offset_by_one),
+    "store_next_slot": ("kvcache_store", _store_next_slot),
+    "bf16_shift_8": ("bf16_to_f64", lambda b: (np.asarray(b, np.uint16).astype(np.uint32) << 8)
+                     .view(np.float32).astype(np.float64)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(monkeypatch, name):
+    attr, fn = MUTATIONS[name]
+    with np.errstate(all="ignore"):
+        failed = _caught(monkeypatch, attr, fn)
+    assert failed, f"no pin caught the planted mistake {name}"

@@ -1,0 +1,282 @@
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+A step is one pass of the hot path over one batch: kvcache_store of the new
+token of each sequence, then paged_decode, on the Qwen3-0.6B-shaped decode
+workload (64 sequences, 16 query / 8 KV heads, head_dim 128, block 256,
+context lengths uniform on [128, 4096], 2048-block pool).  Inputs are seeded
+synthetic bf16 N(0, 1) values resident in HBM before timing starts.
+
+Before every timed step a 512 MiB fill evicts the 256 MB Infinity Cache and
+the L2s (outside the timed events), so each step reads its K/V from HBM.
+Per-step times come from HIP events on the stream the kernels run on.
+
+Prints one JSON line.  Extra legs: the prefix-hit prefill workload (16 x 512
+new tokens over prefixes of up to 3584 tokens) timed the same way, and the
+CPU oracle timed on a bounded sample of the decode workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, published
+FLUSH_BYTES = 512 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run one 1 GiB device copy first (calibrates HBM byte counters)")
+    ap.add_argument("--traffic", type=str, default=None,
+                    help="JSON file with counter-derived HBM bytes per decode launch")
+    return ap.parse_args()
+
+
+def decode_algorithmic_bytes(c) -> int:
+    """Bytes a decode launch must move: K/V of every context token, q, out (bf16), tables, lens."""
+    ctx = c.context_lens.astype(np.int64)
+    kv = int(ctx.sum()) * 2 * c.num_kv_heads * c.head_dim * 2
+    qo = 2 * c.batch * c.num_q_heads * c.head_dim * 2
+    tables = 4 * int(((ctx + c.block_size - 1) // c.block_size).sum()) + 4 * c.batch
+    return kv + qo + tables
+
+
+def store_bytes(c) -> int:
+    return 2 * 2 * c.batch * c.num_kv_heads * c.head_dim * 2 + 4 * c.batch
+
+
+def timed_loop(torch, fn_pre, fn_main, steps, warmup, flush):
+    """Time `steps` passes of fn_pre + fn_main, each preceded by a cache flush.
+
+    Returns (step_ms, main_ms, per_step_main_ms, wall_s):
+      step_ms  mean of fn_pre + fn_main, from back-to-back passes bracketed by two
+               events, minus the same number of back-to-back flushes (so the ~5 us
+               an event record adds to the queue is not charged to the kernels);
+      main_ms  the same for fn_main alone;
+      per_step_main_ms  fn_main bracketed by its own events, one value per pass
+               (each includes one event's overhead): the distribution;
+      wall_s   host wall time of the amortised passes, synchronize on both sides.
+    """
+    for _ in range(warmup):
+        flush()
+        fn_pre()
+        fn_main()
+    torch.cuda.synchronize()
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    e = [ev() for _ in range(6)]
+    t0 = time.perf_counter()
+    e[0].record()
+    for _ in range(steps):
+        flush()
+        fn_pre()
+        fn_main()
+    e[1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    e[2].record()
+    for _ in range(steps):
+        flush()
+        fn_main()
+    e[3].record()
+    for _ in range(steps):
+        flush()
+    e[4].record()
+    torch.cuda.synchronize()
+    t_flush = e[3].elapsed_time(e[4]) / steps
+    step_ms = e[0].elapsed_time(e[1]) / steps - t_flush
+    main_ms = e[2].elapsed_time(e[3]) / steps - t_flush
+    pairs = [(ev(), ev()) for _ in range(steps)]
+    for a, b in pairs:
+        flush()
+        fn_pre()
+        a.record()
+        fn_main()
+        b.record()
+    torch.cuda.synchronize()
+    per_step = [a.elapsed_time(b) for a, b in pairs]
+    return step_ms, main_ms, per_step, wall
+
+
+def cpu_baseline(c, kc, vc, budget_s):
+    """The oracle (as is) on the decode workload, sequence by sequence, within a time budget.
+
+    Sequences are taken in order, wrapping around, until the budget is spent;
+    the result is KV bytes (and sequences) per second of oracle time.
+    """
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    done, t_used, kv, tokens = 0, 0.0, 0, 0
+    while t_used < budget_s:
+        i = done % c.batch
+        t = time.perf_counter()
+        oracle.paged_decode(c.q[i:i + 1], kc, vc, c.block_tables[i:i + 1],
+                            c.context_lens[i:i + 1], np.float32(c.scale))
+        t_used += time.perf_counter() - t
+        kv += int(c.context_lens[i]) * 2 * c.num_kv_heads * c.head_dim * 2
+        tokens += int(c.context_lens[i])
+        done += 1
+    return {"value": round(kv / t_used / 1e9, 4), "unit": "GB/s", "cores": int(cores),
+            "kind": "oracle", "sequences_per_s": round(done / t_used, 2),
+            "sample": f"{done} sequence decodes of the 64-sequence decode workload, taken in "
+                      f"order with wrap-around ({tokens} context tokens), {t_used:.1f} s of oracle time"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this library has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import paged_kv_cache_86_amd as pa
+    from workloads import config
+
+    dev = torch.device("cuda:0")
+    pa.load_library()
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    # A read of 512 MiB replaces the 256 MB Infinity Cache's contents with clean
+    # lines (a write would leave dirty lines whose write-back competes with the
+    # next step's reads).
+    flush_buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+
+    def flush():
+        flush_buf.sum()
+
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ---------------------------------------------------------------- decode (headline)
+    c = config(2)
+    kc, vc = bf16(c.k_cache), bf16(c.v_cache)
+    q, k_new, v_new = bf16(c.q), bf16(c.k_new), bf16(c.v_new)
+    slots, tables, ctx = i32(c.slot_mapping), i32(c.block_tables), i32(c.context_lens)
+    out = torch.empty((c.batch, c.num_q_heads, c.head_dim), dtype=torch.bfloat16, device=dev)
+    ws = pa.decode_workspace(pa.decode_workspace_bytes(c.batch, c.num_q_heads, c.num_kv_heads,
+                                                       c.head_dim, c.block_size,
+                                                       c.max_blocks_per_seq), dev)
+
+    def store():
+        pa.kvcache_store(k_new, v_new, slots, kc, vc)
+
+    def decode():
+        pa.paged_decode(q, kc, vc, tables, ctx, c.scale, out, workspace=ws)
+
+    ms_step, ms_dec, dec_ms, wall = timed_loop(torch, store, decode, args.steps, args.warmup,
+                                               flush)
+    kv_bytes = c.kv_bytes()
+    alg = decode_algorithmic_bytes(c)
+    achieved = alg / (ms_dec * 1e-3) / 1e9
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        traffic = json.load(open(args.traffic)).get("decode_bytes_per_launch")
+
+    result = {
+        "metric": "paged-decode KV GB/s (% of HBM peak) and tokens/s at batch 64, ctx <=4096",
+        "value": round(kv_bytes / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen3-0.6b-shaped paged decode: store + decode, batch 64, "
+                               "16 q / 8 kv heads, head_dim 128, block 256, ctx U[128,4096]",
+                   "batch": c.batch, "num_q_heads": c.num_q_heads, "num_kv_heads": c.num_kv_heads,
+                   "head_dim": c.head_dim, "block_size": c.block_size,
+                   "num_blocks": c.num_blocks, "context_tokens": int(c.context_lens.sum()),
+                   "seed": c.seed},
+        "pct_hbm_peak": round(100 * kv_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(c.batch / (ms_step * 1e-3), 1),
+        "decode_ms": round(ms_dec, 5),
+        "decode_ms_per_call_events": {"min": round(float(np.min(dec_ms)), 5),
+                                      "median": round(float(np.median(dec_ms)), 5),
+                                      "p90": round(float(np.percentile(dec_ms, 90)), 5)},
+        "store_ms": round(ms_step - ms_dec, 5),
+        "wall_s_timed_region_incl_flush": round(wall, 4),
+        "roofline": {"kernel": "paged_decode_kernel", "bound": "hbm",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": alg},
+    }
+
+    # ---------------------------------------------------------------- prefill (extra leg)
+    if not args.no_prefill:
+        p = config(5)
+        pk, pv = bf16(p.k_cache), bf16(p.v_cache)
+        pq, pkn, pvn = bf16(p.q), bf16(p.k_new), bf16(p.v_new)
+        pcu, pbt, pctx = i32(p.cu_seqlens_q), i32(p.block_tables), i32(p.context_lens)
+        pslots = i32(p.slot_mapping)
+        pout = torch.empty((p.total_q, p.num_q_heads, p.head_dim), dtype=torch.bfloat16, device=dev)
+        mq = int(p.q_lens.max())
+
+        def pstore():
+            pa.kvcache_store(pkn, pvn, pslots, pk, pv)
+
+        def prefill():
+            pa.paged_prefill(pq, pkn, pvn, pcu, pbt, pctx, pout, k_cache=pk, v_cache=pv,
+                             scale=p.scale, max_q_len=mq)
+
+        try:
+            pstep, pms, pev, _ = timed_loop(torch, pstore, prefill, max(10, args.steps // 2),
+                                            max(3, args.warmup // 2), flush)
+            tf = p.flops() / (pms * 1e-3) / 1e12
+            result["prefill"] = {
+                "workload": "prefix-hit prefill: 16 seqs x 512 new tokens, prefix U[0,3584], "
+                            "16 q / 8 kv heads, head_dim 128, block 256",
+                "ms": round(pms, 5), "ms_step_incl_store": round(pstep, 5),
+                "ms_per_call_events_median": round(float(np.median(pev)), 5),
+                "tflops": round(tf, 2), "flops_per_launch": p.flops(),
+                "mfma_util": round(tf / MFMA_BF16_PEAK_TFS, 4),
+                "new_tokens_per_s": round(p.total_q / (pstep * 1e-3), 1)}
+        except Exception as e:  # prefill not available: report, do not hide the decode result
+            result["prefill"] = {"error": str(e)}
+
+    # ---------------------------------------------------------------- CPU oracle
+    if not args.no_cpu_baseline:
+        import oracle
+        okc, ovc = oracle.kvcache_store(c.k_new, c.v_new, c.slot_mapping, c.k_cache, c.v_cache)
+        result["cpu_baseline"] = cpu_baseline(c, okc, ovc, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,156 @@
+/*
+ * libpagedattn — attention over a paged KV cache on AMD Instinct MI355X (gfx950).
+ *
+ * The three operations are the ones a minimal vLLM engine runs inside every
+ * attention layer, as described in the MinivLLM guide "vLLM 技术路线"
+ * (Step 4 §4.4 allocate_kv_cache, §4.5 prepare_prefill / prepare_decode,
+ * §4.6 run_model) and in "Nano-vLLM源码学习(2)" §2 Config (decode and
+ * prefix-hit prefill both read paged KV through a block table):
+ *
+ *   pa_kvcache_store   write the new tokens' K/V rows into cache slots (slot_mapping)
+ *   pa_paged_decode    one query token per sequence over its paged context
+ *   pa_paged_prefill   a chunk of new tokens over a cached prefix plus itself, causal
+ *
+ * plus pa_paged_gather, a test aid that un-pages a cache through the block tables.
+ *
+ * Common conventions
+ * ------------------
+ * - Every tensor pointer is a DEVICE pointer to a dense row-major buffer that
+ *   the caller owns.  No call allocates, frees or synchronizes; every call is
+ *   asynchronous on `stream` (a hipStream_t; NULL = the null stream).
+ * - bf16 = IEEE bfloat16 bit patterns; indices are int32.
+ * - KV cache layout: K and V are separate pools [num_blocks, block_size,
+ *   num_kv_heads, head_dim]; the flat slot s = block_id * block_size + offset
+ *   addresses row [s / block_size, s % block_size, :, :] (MinivLLM guide
+ *   §4.5: a block is kv_cache[..., b*bs:(b+1)*bs, ...], and the decode slot is
+ *   block_table[-1] * block_size + last_block_num_tokens - 1).
+ * - block_tables [B, max_blocks_per_seq]: logical block j of sequence i lives
+ *   in physical block block_tables[i][j] (VLLM 0.7.3 source article §3.1).
+ *   Entries past ceil(context_len / block_size) are never read (pad with -1).
+ * - GQA: query head h reads KV head h / (num_q_heads / num_kv_heads).
+ * - Supported: head_dim in {64, 128}; block_size a power of two in [1, 1024];
+ *   num_q_heads a multiple of num_kv_heads.  Decode additionally needs
+ *   max_blocks_per_seq * block_size <= 65536 tokens at head_dim 128 (131072
+ *   at head_dim 64): 256 splits of 256 (512) tokens.
+ * - Return value: PA_OK, or a negative pa_status.  Argument errors are found
+ *   on the host before anything is launched.  PA_ERR_HIP reports a failed
+ *   launch (the HIP error is left for the caller's next HIP call to see).
+ * - Device-data preconditions (not checked on the host): slots unique within
+ *   a call; table entries for read blocks in [0, num_blocks); context_len <=
+ *   max_blocks_per_seq * block_size.  The kernels never touch memory outside
+ *   the buffers when these are violated: out-of-range slots are skipped,
+ *   out-of-range block ids drop their tokens from the softmax, and context
+ *   lengths are clamped to the table width.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required pointer is NULL */
+  PA_ERR_SHAPE = -2,       /* a size is negative/zero where it may not be, or inconsistent */
+  PA_ERR_UNSUPPORTED = -3, /* head_dim / block_size / dtype outside the supported set */
+  PA_ERR_WORKSPACE = -4,   /* decode workspace missing or too small */
+  PA_ERR_HIP = -5          /* a kernel launch failed */
+} pa_status;
+
+typedef enum { PA_BF16 = 0, PA_F32 = 1 } pa_dtype; /* output element type */
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* pa_status_string(int status);
+
+/*
+ * KV store (MinivLLM guide §4.4-4.5: slot_mapping records where each new
+ * token's K/V is written; only uncached tokens get a slot; §4.6: padded rows
+ * carry a sentinel).
+ *   k, v          [T, num_kv_heads, head_dim] bf16, read
+ *   slot_mapping  [T] int32; slot < 0 (padding) or >= num_blocks*block_size writes nothing
+ *   k_cache, v_cache [num_blocks, block_size, num_kv_heads, head_dim] bf16, updated in place
+ * A bit-exact copy of each row.  T == 0 is a no-op.
+ */
+int pa_kvcache_store(const void* k, const void* v, const int32_t* slot_mapping, int T,
+                     void* k_cache, void* v_cache, int num_blocks, int block_size,
+                     int num_kv_heads, int head_dim, void* stream);
+
+/*
+ * Bytes of scratch pa_paged_decode needs for these sizes (0 if the sizes are
+ * invalid).  The workspace holds split-K partial results (a running max and
+ * sum per query head and split, then the unnormalised outputs); it needs no
+ * initialisation and keeps nothing between calls.  Calls that may run
+ * concurrently need separate workspaces.
+ */
+size_t pa_paged_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
+                                       int head_dim, int block_size, int max_blocks_per_seq);
+
+/*
+ * Paged decode (MinivLLM guide §4.5 prepare_decode, §4.6 run_model;
+ * "Nano-vLLM源码学习(2)" §2: the decode path reads paged KV via block_table).
+ *   q             [B, num_q_heads, head_dim] bf16
+ *   k_cache, v_cache [num_blocks, block_size, num_kv_heads, head_dim] bf16
+ *   block_tables  [B, max_blocks_per_seq] int32
+ *   context_lens  [B] int32: keys of sequence i are its logical tokens 0..ctx-1
+ *                 (the token being decoded included); ctx <= 0 marks a padded
+ *                 row whose output is all zeros
+ *   scale         multiplies q.k (fp32); scale <= 0 selects 1/sqrt(head_dim)
+ *   out           [B, num_q_heads, head_dim], bf16 (round to nearest even) or fp32
+ *   workspace     see pa_paged_decode_workspace_bytes
+ * out[i,h] = softmax(scale * q[i,h] . K_i^T) V_i, fp32 accumulation.
+ * Deterministic: the same inputs give bit-identical outputs.  Runs as one or
+ * two kernels on `stream` (partials, then a merge when a context spans
+ * more than one split).
+ */
+int pa_paged_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, int max_blocks_per_seq,
+                    const int32_t* context_lens, int num_seqs, int num_q_heads,
+                    int num_kv_heads, int head_dim, int block_size, int num_blocks, float scale,
+                    void* out, int out_dtype, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/*
+ * Prefix-hit prefill ("Nano-vLLM源码学习(2)" §2: the prefix-hit prefill path
+ * reads the cached prefix through block_table; MinivLLM guide §4.5: the batch
+ * is flattened and delimited by cu_seqlens_q, e.g. [0, 3, 5, 9]).
+ *   q             [total_q, num_q_heads, head_dim] bf16
+ *   k_new, v_new  [total_q, num_kv_heads, head_dim] bf16: K/V of the new tokens
+ *   cu_seqlens_q  [B+1] int32 (device), cu_seqlens_q[0] = 0, cu_seqlens_q[B] = total_q
+ *   max_q_len     host-known upper bound of any q_len (sizes the grid)
+ *   k_cache, v_cache, block_tables: the cached prefix, as for decode
+ *   context_lens  [B] int32 = prefix_len + q_len per sequence
+ * Chunk token t of sequence i sits at absolute position P_i + t, P_i =
+ * context_lens[i] - q_len_i, and attends to keys 0..P_i+t: keys below P_i are
+ * read from the cache, the rest from k_new/v_new.  The new tokens need not
+ * have been stored yet.  out is [total_q, num_q_heads, head_dim], bf16 or fp32.
+ */
+int pa_paged_prefill(const void* q, const void* k_new, const void* v_new,
+                     const int32_t* cu_seqlens_q, int num_seqs, int total_q, int max_q_len,
+                     const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                     int max_blocks_per_seq, const int32_t* context_lens, int num_q_heads,
+                     int num_kv_heads, int head_dim, int block_size, int num_blocks, float scale,
+                     void* out, int out_dtype, void* stream);
+
+/*
+ * Test aid: un-page one cache (MinivLLM guide §4.5 block_tables).
+ *   cache         [num_blocks, block_size, num_kv_heads, head_dim] bf16
+ *   cu_seqlens_k  [B+1] int32 (device): prefix sums of context_lens
+ *   out           [cu_seqlens_k[B], num_kv_heads, head_dim] bf16:
+ *                 out[cu_seqlens_k[i] + j] = cache row of logical token j of sequence i
+ *   max_context_len  host-known upper bound of any context_len (sizes the grid)
+ * Bit-exact copy; rows of tokens whose block id is out of range are left untouched.
+ */
+int pa_paged_gather(const void* cache, const int32_t* block_tables, int max_blocks_per_seq,
+                    const int32_t* context_lens, const int32_t* cu_seqlens_k, int num_seqs,
+                    int max_context_len, int num_kv_heads, int head_dim, int block_size,
+                    int num_blocks, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

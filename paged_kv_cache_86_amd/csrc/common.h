@@ -1,0 +1,53 @@
+// Shared device helpers for the gfx950 kernels of libpagedattn.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 8 bf16 = one 128-bit load
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+// Running-max start value: finite, so exp2(m_old - m_new) never sees inf - inf.
+constexpr float kNegBig = -3.0e38f;
+
+__device__ __forceinline__ float bf16lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+// float -> bfloat16 bits, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Two bf16 products summed into an fp32 accumulator (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+
+// Sum over aligned groups of N lanes (N = 8 or 16) inside a DPP row; every lane
+// of the group ends up holding the group total.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+  v += dpp<0x141>(v);  // row_half_mirror: quads 0<->1 inside each 8
+  if constexpr (N == 16) v += dpp<0x140>(v);  // row_mirror: halves 0<->1 inside 16
+  return v;
+}
+
+__device__ __forceinline__ float shfl_xor(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+}  // namespace pa

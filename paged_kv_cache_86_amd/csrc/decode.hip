@@ -1,0 +1,425 @@
+// Paged decode attention for gfx950: one query token per sequence reads its
+// K/V through the block table (MinivLLM guide "vLLM 技术路线", Step 4 §4.5
+// prepare_decode and §4.6 run_model; "Nano-vLLM源码学习(2)" §2, the decode
+// path reads paged KV via block_table).
+//
+// Work decomposition (this library's design, not the pages'):
+//   * one workgroup (4 waves) per (sequence, KV head [sub-group], split of
+//     2^split_log2 tokens); all query heads sharing that KV head (GQA) are
+//     served from the same K/V registers, so each K/V byte is read once;
+//   * a wave walks chunks of U*RPW tokens: RPW rows per 64-lane load with
+//     D/8 lanes per row, each lane loading 16 contiguous bytes (fully
+//     coalesced 128-bit loads; a row of one head is D*2 contiguous bytes);
+//   * q.k uses v_dot2_f32_bf16 on the packed bf16 pairs, reduced across the
+//     lanes of a row with DPP; each row slot keeps its own online-softmax
+//     state (running max, sum, fp32 accumulator) so the loop has no
+//     cross-row traffic; states are merged once at the end (shuffles, then
+//     LDS across waves);
+//   * split-K partials (m, l, unnormalised o) go to the workspace and a
+//     second, small kernel merges them in split order (deterministic); a
+//     context that fits in one split writes its output directly.  The
+//     kernel boundary is what makes one XCD's partials visible to another:
+//     an in-kernel "last workgroup merges" scheme needs a device-scope
+//     release/acquire per workgroup, which on this chip writes back and
+//     invalidates the whole L2 of an XCD and costs far more than a launch.
+#include "common.h"
+#include "kernels.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kMaxSplitBlocks = 512;  // split tokens / block size (block size >= 1)
+
+// One workgroup = one (sequence, head group, split).  A split is
+// kWaves * NIT chunks of U * RPW tokens; wave w takes chunks w, w + 4, ...
+// The chunk loop is fully unrolled so that every K/V load of the wave can be
+// issued before the first one is consumed.
+template <int D, int GT, int U, int NIT, bool PRELOAD, bool NT>
+__global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
+  constexpr int LPR = D / 8;     // lanes per K/V row of one head (16 bytes each)
+  constexpr int RPW = 64 / LPR;  // rows per 64-lane load
+  constexpr int CH = U * RPW;    // tokens per wave chunk
+  constexpr int S = kWaves * NIT * CH;  // tokens per split
+
+  __shared__ int s_blk[kMaxSplitBlocks];
+  __shared__ float s_m[kWaves][GT];
+  __shared__ float s_l[kWaves][GT];
+  __shared__ float s_acc[kWaves][GT][D];
+
+  const int bid = blockIdx.x;
+  const int hg = bid % a.hg;
+  const int rest = bid / a.hg;
+  const int split = rest % a.nsplit_max;
+  const int seq = rest / a.nsplit_max;
+  const int kvh = hg / a.nsub;
+  const int sub = hg - kvh * a.nsub;
+  const int h0 = kvh * a.group + sub * GT;
+  const int gh = min(GT, a.group - sub * GT);
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int r = lane / LPR;
+  const int c = lane - r * LPR;
+  const int t0 = split * S;
+  const int b0 = t0 >> a.bs_log2;
+
+  // Issued before the context length is known, so the three loads overlap:
+  // table entries of this split (clamped to the table row), q, context length.
+  const int nb_max = S > (1 << a.bs_log2) ? (S >> a.bs_log2) : 1;
+#pragma unroll
+  for (int k = 0; k < kMaxSplitBlocks / 256; ++k) {
+    const int i = tid + 256 * k;
+    if (i < nb_max) {
+      int blk = -1;
+      if (b0 + i < a.mbs) blk = a.block_tables[(int64_t)seq * a.mbs + b0 + i];
+      s_blk[i] = (blk >= 0 && blk < a.num_blocks) ? blk : -1;
+    }
+  }
+  // Heads past the group's end (last sub-group) re-read its last head; their
+  // results are never stored.
+  u32x4 qv[GT];
+#pragma unroll
+  for (int h = 0; h < GT; ++h) {
+    const int hh = h < gh ? h : gh - 1;
+    qv[h] = *(const u32x4*)(a.q + ((int64_t)seq * a.Hq + h0 + hh) * D + c * 8);
+  }
+  int ctx = a.context_lens[seq];
+  const int cap = a.mbs << a.bs_log2;
+  ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+
+  if (ctx == 0) {  // padded row: output zeros
+    if (split == 0) {
+      for (int i = tid; i < gh * D; i += blockDim.x) {
+        const int64_t o = ((int64_t)seq * a.Hq + h0) * D + i;
+        if (a.out_f32) ((float*)a.out)[o] = 0.f;
+        else ((uint16_t*)a.out)[o] = 0;
+      }
+    }
+    return;
+  }
+  const int nsplit = (ctx + S - 1) / S;
+  if (split >= nsplit) return;
+  const int t1 = min(ctx, t0 + S);
+  __syncthreads();
+
+  const int64_t row_stride = (int64_t)a.Hkv * D;
+  const int64_t head_off = (int64_t)kvh * D + c * 8;
+  const int bs_mask = (1 << a.bs_log2) - 1;
+
+  float m[GT], l[GT], acc[GT][8];
+#pragma unroll
+  for (int h = 0; h < GT; ++h) {
+    m[h] = kNegBig;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  }
+
+  auto load_chunk = [&](int it, u32x4 (&kc)[U], u32x4 (&vc)[U], bool (&ok)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      // Rows past the split end re-read the split's last row (in bounds, finite) and
+      // are masked out of the softmax below.
+      const int j = t0 + (it * kWaves + w) * CH + u * RPW + r;
+      const int jj = j < t1 ? j : t1 - 1;
+      int blk = s_blk[(jj >> a.bs_log2) - b0];
+      ok[u] = (j < t1) && (blk >= 0);
+      blk = blk < 0 ? 0 : blk;
+      const int64_t off = (((int64_t)blk << a.bs_log2) + (jj & bs_mask)) * row_stride + head_off;
+      if constexpr (NT) {
+        kc[u] = __builtin_nontemporal_load((const u32x4*)(a.k_cache + off));
+        vc[u] = __builtin_nontemporal_load((const u32x4*)(a.v_cache + off));
+      } else {
+        kc[u] = *(const u32x4*)(a.k_cache + off);
+        vc[u] = *(const u32x4*)(a.v_cache + off);
+      }
+    }
+  };
+
+  // PRELOAD issues every load of the wave before the first is used; otherwise
+  // each chunk is loaded at the top of its iteration.
+  u32x4 kpre[PRELOAD ? NIT : 1][U], vpre[PRELOAD ? NIT : 1][U];
+  bool okpre[PRELOAD ? NIT : 1][U];
+  if constexpr (PRELOAD) {
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) load_chunk(it, kpre[it], vpre[it], okpre[it]);
+  }
+
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    u32x4 kc[U], vc[U];
+    bool ok[U];
+    if constexpr (PRELOAD) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        kc[u] = kpre[it][u];
+        vc[u] = vpre[it][u];
+        ok[u] = okpre[it][u];
+      }
+    } else {
+      load_chunk(it, kc, vc, ok);
+    }
+
+    float s[U][GT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        float d = dot2_bf16(qv[h].x, kc[u].x, 0.f);
+        d = dot2_bf16(qv[h].y, kc[u].y, d);
+        d = dot2_bf16(qv[h].z, kc[u].z, d);
+        d = dot2_bf16(qv[h].w, kc[u].w, d);
+        d = group_sum<LPR>(d);
+        s[u][h] = ok[u] ? d * a.scale_log2e : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      float mx = s[0][h];
+#pragma unroll
+      for (int u = 1; u < U; ++u) mx = fmaxf(mx, s[u][h]);
+      const float mnew = fmaxf(m[h], mx);
+      const float alpha = __builtin_amdgcn_exp2f(m[h] - mnew);
+      m[h] = mnew;
+      float psum = 0.f;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        s[u][h] = __builtin_amdgcn_exp2f(s[u][h] - mnew);
+        psum += s[u][h];
+      }
+      l[h] = l[h] * alpha + psum;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      // Masked rows contribute p = 0; zeroing V as well keeps a NaN in an
+      // unused slot from turning 0 * NaN into NaN.
+      const uint32_t vw[4] = {ok[u] ? vc[u].x : 0u, ok[u] ? vc[u].y : 0u,
+                              ok[u] ? vc[u].z : 0u, ok[u] ? vc[u].w : 0u};
+      float vf[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vf[2 * e] = bf16lo(vw[e]);
+        vf[2 * e + 1] = bf16hi(vw[e]);
+      }
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(s[u][h], vf[e], acc[h][e]);
+      }
+    }
+  }
+
+  // Merge the row slots of this wave (lanes differing in the row bits).
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) {
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      const float mo = shfl_xor(m[h], off);
+      const float lo = shfl_xor(l[h], off);
+      const float mn = fmaxf(m[h], mo);
+      const float a1 = __builtin_amdgcn_exp2f(m[h] - mn);
+      const float a2 = __builtin_amdgcn_exp2f(mo - mn);
+      l[h] = l[h] * a1 + lo * a2;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float ao = shfl_xor(acc[h][e], off);
+        acc[h][e] = acc[h][e] * a1 + ao * a2;
+      }
+      m[h] = mn;
+    }
+  }
+  if (r == 0) {
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_acc[w][h][c * 8 + e] = acc[h][e];
+      if (c == 0) {
+        s_m[w][h] = m[h];
+        s_l[w][h] = l[h];
+      }
+    }
+  }
+  __syncthreads();
+
+  const int64_t unit = (int64_t)seq * a.hg + hg;
+  for (int i = tid; i < GT * D; i += blockDim.x) {
+    const int h = i / D;
+    const int d = i - h * D;
+    float M = s_m[0][h];
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, s_m[ww][h]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float f = __builtin_amdgcn_exp2f(s_m[ww][h] - M);
+      L += s_l[ww][h] * f;
+      O += s_acc[ww][h][d] * f;
+    }
+    if (nsplit == 1) {
+      if (h < gh) {
+        const int64_t o = ((int64_t)seq * a.Hq + h0 + h) * D + d;
+        const float val = L > 0.f ? O / L : 0.f;
+        if (a.out_f32) ((float*)a.out)[o] = val;
+        else ((uint16_t*)a.out)[o] = (uint16_t)f32_to_bf16_rne(val);
+      }
+    } else {
+      const int64_t p = (unit * a.nsplit_max + split) * GT + h;
+      a.ws_o[p * D + d] = O;
+      if (d == 0) {
+        a.ws_ml[2 * p] = M;
+        a.ws_ml[2 * p + 1] = L;
+      }
+    }
+  }
+}
+
+// Merge the split-K partials of one (sequence, head group):
+// out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), M = max_s m_s, in split order.
+// The partial outputs of the first kCombineChunk splits and every split's
+// (m, l) are loaded before the context length is known (entries past the
+// sequence's last split are read but ignored), so for contexts of up to
+// kCombineChunk splits the merge costs one memory round trip.
+constexpr int kCombineChunk = 16;
+
+template <int D, int GT, int S>
+__global__ __launch_bounds__(256) void paged_decode_combine_kernel(DecodeArgs a) {
+  constexpr int ITEMS = (GT * D + 255) / 256;  // (head, dim) outputs per thread
+  __shared__ float s_w[kDecodeMaxSplits][GT];  // per split: 2^(m_s - M) / L
+  __shared__ float s_ml[kDecodeMaxSplits][GT][2];
+  const int unit = blockIdx.x;
+  const int hg = unit % a.hg;
+  const int seq = unit / a.hg;
+  const int tid = threadIdx.x;
+  const int64_t p0 = (int64_t)unit * a.nsplit_max * GT;
+
+  float pre[ITEMS][kCombineChunk];
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) {
+    const int i = min(tid + 256 * k, GT * D - 1);
+    const int h = i / D;
+    const int d = i - h * D;
+#pragma unroll
+    for (int sp = 0; sp < kCombineChunk; ++sp) {
+      const int spc = min(sp, a.nsplit_max - 1);
+      pre[k][sp] = a.ws_o[(p0 + (int64_t)spc * GT + h) * D + d];
+    }
+  }
+  for (int i = tid; i < a.nsplit_max * GT; i += blockDim.x) {
+    s_ml[i / GT][i % GT][0] = a.ws_ml[2 * (p0 + i)];
+    s_ml[i / GT][i % GT][1] = a.ws_ml[2 * (p0 + i) + 1];
+  }
+  int ctx = a.context_lens[seq];
+  const int cap = a.mbs << a.bs_log2;
+  ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+  const int nsplit = (ctx + S - 1) / S;
+  if (nsplit <= 1) return;  // written directly by the main kernel
+  const int kvh = hg / a.nsub;
+  const int sub = hg - kvh * a.nsub;
+  const int h0 = kvh * a.group + sub * GT;
+  const int gh = min(GT, a.group - sub * GT);
+  __syncthreads();
+  if (tid < GT) {
+    const int h = tid;
+    float M = kNegBig;
+    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, s_ml[sp][h][0]);
+    float L = 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) L += s_ml[sp][h][1] * __builtin_amdgcn_exp2f(s_ml[sp][h][0] - M);
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) s_w[sp][h] = __builtin_amdgcn_exp2f(s_ml[sp][h][0] - M) * inv;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) {
+    const int i = tid + 256 * k;
+    if (i >= gh * D) continue;
+    const int h = i / D;
+    const int d = i - h * D;
+    float O = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < kCombineChunk; ++sp)
+      if (sp < nsplit) O += pre[k][sp] * s_w[sp][h];
+    for (int sp = kCombineChunk; sp < nsplit; ++sp)
+      O += a.ws_o[(p0 + (int64_t)sp * GT + h) * D + d] * s_w[sp][h];
+    const int64_t o = ((int64_t)seq * a.Hq + h0 + h) * D + d;
+    if (a.out_f32) ((float*)a.out)[o] = O;
+    else ((uint16_t*)a.out)[o] = (uint16_t)f32_to_bf16_rne(O);
+  }
+}
+
+// Production tiling (measured on the Qwen3-0.6B-shaped decode, 64 x 16/8 heads,
+// contexts up to 4096): U = 2 rows per lane per chunk, NIT = 8 chunks per wave,
+// every load issued up front, non-temporal (streaming) loads.  That is
+// 256-token splits at D = 128 and 512-token splits at D = 64.
+constexpr int kU = 2;
+constexpr int kNit = 8;
+constexpr bool kPreload = true;
+constexpr bool kNontemporal = true;
+
+template <int D>
+constexpr int split_tokens() { return kWaves * kNit * kU * (64 / (D / 8)); }
+
+template <int D, int GT>
+int launch_d(const DecodeArgs& a, int B, hipStream_t stream) {
+  const int64_t nwg = (int64_t)B * a.hg * a.nsplit_max;
+  hipLaunchKernelGGL((paged_decode_kernel<D, GT, kU, kNit, kPreload, kNontemporal>), dim3((unsigned)nwg), dim3(256), 0,
+                     stream, a);
+  if (hipGetLastError() != hipSuccess) return -1;
+  if (a.nsplit_max > 1) {
+    hipLaunchKernelGGL((paged_decode_combine_kernel<D, GT, split_tokens<D>()>),
+                       dim3((unsigned)((int64_t)B * a.hg)), dim3(256), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return -1;
+  }
+  return 0;
+}
+
+template <int D>
+int launch_gt(const DecodeArgs& a, int B, int gt, hipStream_t stream) {
+  switch (gt) {
+    case 1: return launch_d<D, 1>(a, B, stream);
+    case 2: return launch_d<D, 2>(a, B, stream);
+    case 3: return launch_d<D, 3>(a, B, stream);
+    case 4: return launch_d<D, 4>(a, B, stream);
+    case 5: return launch_d<D, 5>(a, B, stream);
+    case 6: return launch_d<D, 6>(a, B, stream);
+    case 7: return launch_d<D, 7>(a, B, stream);
+    case 8: return launch_d<D, 8>(a, B, stream);
+    default: return -2;
+  }
+}
+
+}  // namespace
+
+DecodePlan plan_decode(int B, int Hq, int Hkv, int head_dim, int block_size, int mbs) {
+  DecodePlan p{};
+  p.group = Hq / Hkv;
+  p.nsub = (p.group + 7) / 8;
+  p.gt = (p.group + p.nsub - 1) / p.nsub;
+  const int64_t max_ctx = (int64_t)mbs * block_size;
+  const int64_t units = (int64_t)B * Hkv * p.nsub;
+  const int S = head_dim == 64 ? split_tokens<64>() : split_tokens<128>();
+  int sl = 0;
+  while ((1 << sl) < S) ++sl;
+  p.split_log2 = sl;
+  p.nsplit_max = (int)((max_ctx + S - 1) / S);
+  if (p.nsplit_max < 1) p.nsplit_max = 1;
+  const int64_t parts = units * p.nsplit_max * p.gt;
+  auto round256 = [](size_t x) { return (x + 255) / 256 * 256; };
+  p.units = units;
+  p.ml_bytes = round256((size_t)parts * 2 * sizeof(float));
+  p.o_bytes = round256((size_t)parts * head_dim * sizeof(float));
+  return p;
+}
+
+int launch_paged_decode(const DecodeArgs& a, int B, int head_dim, int gt, hipStream_t stream) {
+  if (B == 0) return 0;
+  if (head_dim == 128) return launch_gt<128>(a, B, gt, stream);
+  if (head_dim == 64) return launch_gt<64>(a, B, gt, stream);
+  return -2;
+}
+
+}  // namespace pa

@@ -1,0 +1,71 @@
+// Internal launch interface between the C ABI (pagedattn.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+// Upper bound of (sequence, KV-head group) pairs in one decode call (one
+// combine workgroup each).
+constexpr int64_t kDecodeMaxUnits = 1 << 24;
+// Most splits one decode context may span (the merge stages them in LDS).
+constexpr int kDecodeMaxSplits = 256;
+
+int launch_kvcache_store(const void* k, const void* v, const int32_t* slot_mapping, int T,
+                         void* k_cache, void* v_cache, int num_blocks, int block_size,
+                         int num_kv_heads, int head_dim, hipStream_t stream);
+
+int launch_paged_gather(const void* cache, const int32_t* block_tables, int mbs,
+                        const int32_t* context_lens, const int32_t* cu_seqlens_k, int B,
+                        int max_context_len, int num_kv_heads, int head_dim, int bs_log2,
+                        int num_blocks, void* out, hipStream_t stream);
+
+// Split-K geometry of a decode call; a function of host-known sizes only.
+struct DecodePlan {
+  int group;       // query heads per KV head
+  int nsub;        // workgroups sharing one KV head's query heads
+  int gt;          // query heads handled by one workgroup (<= 8)
+  int split_log2;  // tokens per split = 1 << split_log2
+  int nsplit_max;  // splits of the longest possible context
+  int64_t units;   // (sequence, head group) pairs
+  size_t ml_bytes, o_bytes;  // workspace regions: (max, sum) pairs, then unnormalised outputs
+  size_t workspace_bytes() const { return ml_bytes + o_bytes; }
+};
+
+DecodePlan plan_decode(int B, int Hq, int Hkv, int head_dim, int block_size, int mbs);
+
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  void* out;
+  float* ws_ml;
+  float* ws_o;
+  int mbs, Hq, Hkv, group, nsub, hg, bs_log2, split_log2, nsplit_max, num_blocks, out_f32;
+  float scale_log2e;
+};
+
+int launch_paged_decode(const DecodeArgs& args, int B, int head_dim, int gt, hipStream_t stream);
+
+struct PrefillArgs {
+  const uint16_t* q;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const int32_t* cu_seqlens_q;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  void* out;
+  int B, mbs, Hq, Hkv, group, bs_log2, num_blocks, out_f32, max_q_len;
+  float scale_log2e;
+};
+
+int launch_paged_prefill(const PrefillArgs& args, int head_dim, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,193 @@
+// C ABI of libpagedattn: argument checks, launch geometry, status codes.
+// The operations and their conventions are documented in include/pagedattn.h.
+#include "../../include/pagedattn.h"
+
+#include <math.h>
+
+#include "kernels.h"
+
+namespace {
+
+bool pow2_log2(int x, int* lg) {
+  if (x <= 0 || (x & (x - 1)) != 0) return false;
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  *lg = l;
+  return true;
+}
+
+// Head dim and block size support shared by every call.
+int check_geometry(int num_kv_heads, int head_dim, int block_size, int num_blocks, int* bs_log2) {
+  if (num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (!pow2_log2(block_size, bs_log2) || block_size > 1024) return PA_ERR_UNSUPPORTED;
+  // Every flat slot index and every element offset inside one pool must fit.
+  const int64_t slots = (int64_t)num_blocks * block_size;
+  if (slots > INT32_MAX) return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+float resolve_scale(float scale, int head_dim) {
+  return (scale > 0.f && isfinite(scale)) ? scale : (float)(1.0 / sqrt((double)head_dim));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: invalid or inconsistent size";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: head_dim, block_size or dtype not supported";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: decode workspace missing or too small";
+    case PA_ERR_HIP: return "PA_ERR_HIP: kernel launch failed";
+    default: return "unknown pa_status";
+  }
+}
+
+int pa_kvcache_store(const void* k, const void* v, const int32_t* slot_mapping, int T,
+                     void* k_cache, void* v_cache, int num_blocks, int block_size,
+                     int num_kv_heads, int head_dim, void* stream) {
+  if (T < 0) return PA_ERR_SHAPE;
+  int bs_log2 = 0;
+  const int g = check_geometry(num_kv_heads, head_dim, block_size, num_blocks, &bs_log2);
+  if (g != PA_OK) return g;
+  if (T == 0) return PA_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
+  if ((int64_t)T * num_kv_heads * head_dim / 8 > INT32_MAX) return PA_ERR_SHAPE;
+  return pa::launch_kvcache_store(k, v, slot_mapping, T, k_cache, v_cache, num_blocks, block_size,
+                                  num_kv_heads, head_dim, (hipStream_t)stream) == 0
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+size_t pa_paged_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
+                                       int head_dim, int block_size, int max_blocks_per_seq) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
+      block_size <= 0 || num_q_heads % num_kv_heads != 0)
+    return 0;
+  const pa::DecodePlan p = pa::plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                           block_size, max_blocks_per_seq);
+  return (p.units > pa::kDecodeMaxUnits || p.nsplit_max > pa::kDecodeMaxSplits)
+             ? 0
+             : p.workspace_bytes();
+}
+
+int pa_paged_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, int max_blocks_per_seq,
+                    const int32_t* context_lens, int num_seqs, int num_q_heads,
+                    int num_kv_heads, int head_dim, int block_size, int num_blocks, float scale,
+                    void* out, int out_dtype, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
+  int bs_log2 = 0;
+  const int g = check_geometry(num_kv_heads, head_dim, block_size, num_blocks, &bs_log2);
+  if (g != PA_OK) return g;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (out_dtype != PA_BF16 && out_dtype != PA_F32) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX / 2) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PA_ERR_NULL;
+  const pa::DecodePlan p = pa::plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                           block_size, max_blocks_per_seq);
+  if (!workspace) return PA_ERR_WORKSPACE;
+  if (workspace_bytes < p.workspace_bytes()) return PA_ERR_WORKSPACE;
+  const int64_t hg = (int64_t)num_kv_heads * p.nsub;
+  if ((int64_t)num_seqs * hg * p.nsplit_max > INT32_MAX) return PA_ERR_SHAPE;
+  if (p.units > pa::kDecodeMaxUnits) return PA_ERR_SHAPE;
+  if (p.nsplit_max > pa::kDecodeMaxSplits) return PA_ERR_UNSUPPORTED;
+
+  pa::DecodeArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k_cache = (const uint16_t*)k_cache;
+  a.v_cache = (const uint16_t*)v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.out = out;
+  char* ws = (char*)workspace;
+  a.ws_ml = (float*)ws;
+  a.ws_o = (float*)(ws + p.ml_bytes);
+  a.mbs = max_blocks_per_seq;
+  a.Hq = num_q_heads;
+  a.Hkv = num_kv_heads;
+  a.group = p.group;
+  a.nsub = p.nsub;
+  a.hg = (int)hg;
+  a.bs_log2 = bs_log2;
+  a.split_log2 = p.split_log2;
+  a.nsplit_max = p.nsplit_max;
+  a.num_blocks = num_blocks;
+  a.out_f32 = out_dtype == PA_F32;
+  a.scale_log2e = resolve_scale(scale, head_dim) * pa::kLog2eHost;
+  return pa::launch_paged_decode(a, num_seqs, head_dim, p.gt, (hipStream_t)stream) == 0
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+int pa_paged_prefill(const void* q, const void* k_new, const void* v_new,
+                     const int32_t* cu_seqlens_q, int num_seqs, int total_q, int max_q_len,
+                     const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                     int max_blocks_per_seq, const int32_t* context_lens, int num_q_heads,
+                     int num_kv_heads, int head_dim, int block_size, int num_blocks, float scale,
+                     void* out, int out_dtype, void* stream) {
+  if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || num_q_heads <= 0 ||
+      max_blocks_per_seq <= 0)
+    return PA_ERR_SHAPE;
+  int bs_log2 = 0;
+  const int g = check_geometry(num_kv_heads, head_dim, block_size, num_blocks, &bs_log2);
+  if (g != PA_OK) return g;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (out_dtype != PA_BF16 && out_dtype != PA_F32) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX / 2) return PA_ERR_SHAPE;
+  if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PA_OK;
+  if (!q || !k_new || !v_new || !cu_seqlens_q || !k_cache || !v_cache || !block_tables ||
+      !context_lens || !out)
+    return PA_ERR_NULL;
+  if (max_q_len > total_q) return PA_ERR_SHAPE;
+
+  pa::PrefillArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k_new = (const uint16_t*)k_new;
+  a.v_new = (const uint16_t*)v_new;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.k_cache = (const uint16_t*)k_cache;
+  a.v_cache = (const uint16_t*)v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.out = out;
+  a.B = num_seqs;
+  a.mbs = max_blocks_per_seq;
+  a.Hq = num_q_heads;
+  a.Hkv = num_kv_heads;
+  a.group = num_q_heads / num_kv_heads;
+  a.bs_log2 = bs_log2;
+  a.num_blocks = num_blocks;
+  a.out_f32 = out_dtype == PA_F32;
+  a.max_q_len = max_q_len;
+  a.scale_log2e = resolve_scale(scale, head_dim) * pa::kLog2eHost;
+  const int rc = pa::launch_paged_prefill(a, head_dim, (hipStream_t)stream);
+  if (rc == -3) return PA_ERR_UNSUPPORTED;
+  return rc == 0 ? PA_OK : PA_ERR_HIP;
+}
+
+int pa_paged_gather(const void* cache, const int32_t* block_tables, int max_blocks_per_seq,
+                    const int32_t* context_lens, const int32_t* cu_seqlens_k, int num_seqs,
+                    int max_context_len, int num_kv_heads, int head_dim, int block_size,
+                    int num_blocks, void* out, void* stream) {
+  if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
+  int bs_log2 = 0;
+  const int g = check_geometry(num_kv_heads, head_dim, block_size, num_blocks, &bs_log2);
+  if (g != PA_OK) return g;
+  if (num_seqs > 65535) return PA_ERR_SHAPE;
+  if (num_seqs == 0 || max_context_len == 0) return PA_OK;
+  if (!cache || !block_tables || !context_lens || !cu_seqlens_k || !out) return PA_ERR_NULL;
+  return pa::launch_paged_gather(cache, block_tables, max_blocks_per_seq, context_lens,
+                                 cu_seqlens_k, num_seqs, max_context_len, num_kv_heads, head_dim,
+                                 bs_log2, num_blocks, out, (hipStream_t)stream) == 0
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+}  // extern "C"

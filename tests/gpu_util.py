@@ -1,0 +1,64 @@
+"""Moving seeded NumPy inputs to the GPU and results back (no arithmetic)."""
+import sys
+
+import numpy as np
+import torch
+
+import paged_kv_cache_86_amd as pa
+
+
+def device():
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need a HIP device")
+    pa.load_library()  # fail loudly when the library is not built
+    return torch.device("cuda:0")
+
+
+def bf16(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def i32(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+
+def bits(t) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def as_f64(t) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def say(*msg):
+    print(*msg, flush=True)
+    sys.stdout.flush()
+
+
+class DecodeOnDevice:
+    """A decode workload resident on the GPU (caches before the store)."""
+
+    def __init__(self, c, dev):
+        self.c = c
+        self.dev = dev
+        self.k_cache = bf16(c.k_cache, dev)
+        self.v_cache = bf16(c.v_cache, dev)
+        self.q = bf16(c.q, dev)
+        self.k_new = bf16(c.k_new, dev)
+        self.v_new = bf16(c.v_new, dev)
+        self.slots = i32(c.slot_mapping, dev)
+        self.tables = i32(c.block_tables, dev)
+        self.ctx = i32(c.context_lens, dev)
+
+    def store(self):
+        pa.kvcache_store(self.k_new, self.v_new, self.slots, self.k_cache, self.v_cache)
+
+    def decode(self, out_dtype=torch.float32, tables=None, k_cache=None, v_cache=None,
+               workspace=None):
+        c = self.c
+        out = torch.empty((c.batch, c.num_q_heads, c.head_dim), dtype=out_dtype, device=self.dev)
+        pa.paged_decode(self.q, self.k_cache if k_cache is None else k_cache,
+                        self.v_cache if v_cache is None else v_cache,
+                        self.tables if tables is None else tables, self.ctx, c.scale, out,
+                        workspace=workspace)
+        return out

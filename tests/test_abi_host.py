@@ -1,0 +1,125 @@
+"""The C-ABI library on the host: it loads, exports what the header declares, and rejects
+bad arguments with the documented status codes before anything reaches the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_86_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedattn.h")
+
+PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE = 0, -1, -2, -3, -4
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its host checks
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return pa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(pa.EXPORTED_SYMBOLS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_library_is_gfx950_code():
+    data = open(pa.LIB_PATH, "rb").read()
+    assert b"gfx950" in data
+
+
+def test_status_strings(lib):
+    for code in (PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, -5):
+        assert pa.status_string(code).startswith("PA_")
+    assert pa.status_string(17) == "unknown pa_status"
+
+
+def store(lib, k=FAKE, T=4, NB=8, BS=16, Hkv=2, D=128):
+    return lib.pa_kvcache_store(k, FAKE, FAKE, T, FAKE, FAKE, NB, BS, Hkv, D, None)
+
+
+def test_store_argument_checks(lib):
+    assert store(lib, T=-1) == PA_ERR_SHAPE
+    assert store(lib, D=96) == PA_ERR_UNSUPPORTED
+    assert store(lib, BS=24) == PA_ERR_UNSUPPORTED
+    assert store(lib, BS=2048) == PA_ERR_UNSUPPORTED
+    assert store(lib, NB=0) == PA_ERR_SHAPE
+    assert store(lib, Hkv=0) == PA_ERR_SHAPE
+    assert store(lib, k=None) == PA_ERR_NULL
+    assert store(lib, k=None, T=0) == PA_OK  # empty batch: nothing to do, nothing launched
+
+
+def decode(lib, B=4, Hq=4, Hkv=2, D=128, BS=16, NB=64, MBS=8, q=FAKE, ws=FAKE, ws_bytes=None,
+           out_dtype=0):
+    if ws_bytes is None:
+        ws_bytes = pa.decode_workspace_bytes(max(B, 1), Hq, Hkv if Hkv > 0 else 1, D, BS, MBS)
+    return lib.pa_paged_decode(q, FAKE, FAKE, FAKE, MBS, FAKE, B, Hq, Hkv, D, BS, NB, 0.0, FAKE,
+                               out_dtype, ws, ws_bytes, None)
+
+
+def test_decode_argument_checks(lib):
+    assert decode(lib, Hq=6, Hkv=4) == PA_ERR_SHAPE
+    assert decode(lib, D=256) == PA_ERR_UNSUPPORTED
+    assert decode(lib, BS=12) == PA_ERR_UNSUPPORTED
+    assert decode(lib, out_dtype=7) == PA_ERR_UNSUPPORTED
+    assert decode(lib, B=-1) == PA_ERR_SHAPE
+    assert decode(lib, MBS=0) == PA_ERR_SHAPE
+    assert decode(lib, q=None) == PA_ERR_NULL
+    assert decode(lib, ws=None) == PA_ERR_WORKSPACE
+    assert decode(lib, ws_bytes=16) == PA_ERR_WORKSPACE
+    assert decode(lib, B=0, q=None) == PA_OK
+    assert decode(lib, MBS=4097, BS=16, ws_bytes=1 << 30) == PA_ERR_UNSUPPORTED  # > 65536 tokens
+
+
+def test_decode_workspace_sizes():
+    # Qwen3-0.6B-shaped decode: 64 x 8 head groups, 16 splits of 256 tokens, 2 heads x (128 + 2) floats
+    b = pa.decode_workspace_bytes(64, 16, 8, 128, 256, 16)
+    assert b == 64 * 8 * 16 * 2 * 2 * 4 + 64 * 8 * 16 * 2 * 128 * 4
+    assert pa.decode_workspace_bytes(0, 16, 8, 128, 256, 16) == 0
+    assert pa.decode_workspace_bytes(4, 6, 4, 128, 16, 8) == 0  # 6 % 4 != 0
+    assert pa.decode_workspace_bytes(4, 8, 4, 128, 16, 4097) == 0  # context above 65536 tokens
+    # more query heads per KV head than one workgroup serves: split into sub-groups
+    assert pa.decode_workspace_bytes(2, 32, 2, 64, 16, 4) > pa.decode_workspace_bytes(2, 16, 2, 64, 16, 4)
+
+
+def prefill(lib, B=2, Tq=10, mq=5, q=FAKE, D=128, BS=16, Hq=4, Hkv=2):
+    return lib.pa_paged_prefill(q, FAKE, FAKE, FAKE, B, Tq, mq, FAKE, FAKE, FAKE, 8, FAKE, Hq, Hkv,
+                                D, BS, 64, 0.0, FAKE, 0, None)
+
+
+def test_prefill_argument_checks(lib):
+    assert prefill(lib, B=-1) == PA_ERR_SHAPE
+    assert prefill(lib, mq=11) == PA_ERR_SHAPE
+    assert prefill(lib, D=80) == PA_ERR_UNSUPPORTED
+    assert prefill(lib, Hq=5) == PA_ERR_SHAPE
+    assert prefill(lib, q=None) == PA_ERR_NULL
+    assert prefill(lib, Tq=0, q=None) == PA_OK
+
+
+def test_gather_argument_checks(lib):
+    def gather(B=2, maxc=40, cache=FAKE, BS=16):
+        return lib.pa_paged_gather(cache, FAKE, 4, FAKE, FAKE, B, maxc, 2, 64, BS, 16, FAKE, None)
+    assert gather(B=-3) == PA_ERR_SHAPE
+    assert gather(BS=3) == PA_ERR_UNSUPPORTED
+    assert gather(cache=None) == PA_ERR_NULL
+    assert gather(B=0, cache=None) == PA_OK
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    k = torch.zeros(2, 1, 64, dtype=torch.bfloat16)
+    cache = torch.zeros(4, 16, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device"):
+        pa.kvcache_store(k, k, torch.zeros(2, dtype=torch.int32), cache, cache)

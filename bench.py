@@ -44,8 +44,10 @@ def parse():
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one 1 GiB device copy first (calibrates HBM byte counters)")
-    ap.add_argument("--traffic", type=str, default=None,
-                    help="JSON file with counter-derived HBM bytes per decode launch")
+    ap.add_argument("--traffic", type=str,
+                    default=os.path.join(ROOT, "profiles", "paged_decode_traffic.json"),
+                    help="counter-derived HBM bytes per decode call; used only while the "
+                         "kernel sources still hash to the recorded value")
     return ap.parse_args()
 
 
@@ -56,6 +58,22 @@ def decode_algorithmic_bytes(c) -> int:
     qo = 2 * c.batch * c.num_q_heads * c.head_dim * 2
     tables = 4 * int(((ctx + c.block_size - 1) // c.block_size).sum()) + 4 * c.batch
     return kv + qo + tables
+
+
+def counter_traffic(path):
+    """HBM bytes per decode call from the recorded FETCH_SIZE/WRITE_SIZE runs, or None when
+    the kernel sources changed since the counters were taken."""
+    import hashlib
+    if not path or not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in rec.get("kernel_sources", []):
+        fp = os.path.join(ROOT, f)
+        if not os.path.exists(fp):
+            return None
+        h.update(open(fp, "rb").read())
+    return rec.get("decode_bytes_per_launch") if h.hexdigest() == rec.get("sha256") else None
 
 
 def store_bytes(c) -> int:
@@ -201,9 +219,7 @@ def main():
     kv_bytes = c.kv_bytes()
     alg = decode_algorithmic_bytes(c)
     achieved = alg / (ms_dec * 1e-3) / 1e9
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        traffic = json.load(open(args.traffic)).get("decode_bytes_per_launch")
+    traffic = counter_traffic(args.traffic)
 
     result = {
         "metric": "paged-decode KV GB/s (% of HBM peak) and tokens/s at batch 64, ctx <=4096",
@@ -232,7 +248,8 @@ def main():
                                       "p90": round(float(np.percentile(dec_ms, 90)), 5)},
         "store_ms": round(ms_step - ms_dec, 5),
         "wall_s_timed_region_incl_flush": round(wall, 4),
-        "roofline": {"kernel": "paged_decode_kernel", "bound": "hbm",
+        "roofline": {"kernel": "paged_decode_kernel + paged_decode_combine_kernel (one decode call)",
+                     "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": alg},

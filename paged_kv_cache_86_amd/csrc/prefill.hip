@@ -10,15 +10,21 @@
 // fp32 (flash-attention style):
 //
 //   * a workgroup (4 waves) owns 128 query rows = TT tokens x G heads of one
-//     KV head (GQA rows share every K/V tile), and walks 64-key tiles;
-//   * it computes S^T = K Q^T and O^T = V^T P^T, so the accumulator layout
-//     gives each lane one query row: the softmax is per lane (plus one
-//     exchange with the lane holding the row's other 32 keys) and P feeds the
-//     second MFMA straight from registers, with no trip through LDS;
-//   * the K tile is staged in LDS row-major; the V tile is staged transposed
-//     (V^T rows of 64 keys), with key positions permuted inside each group of
-//     16 (bits 2 and 3 swapped) to match the order in which a lane holds P;
-//   * the next tile's global loads are issued before the current tile's math.
+//     KV head (GQA rows share every K/V tile) and walks 64-key tiles;
+//   * S^T = K Q^T and O^T = V^T P^T: the accumulator layout gives each lane one
+//     query row, so the softmax is per lane (plus one exchange with the lane
+//     holding the row's other 32 keys) and P feeds the second MFMA from
+//     registers; the softmax denominator comes from a third MFMA against a
+//     matrix of ones, so it sums exactly the bf16 weights the PV product uses;
+//   * K and V tiles go straight from global memory to LDS
+//     (global_load_lds_dwordx4), double-buffered, one barrier per tile; rows are
+//     stored with their 16-byte chunks XOR-swizzled so that both the K operand
+//     reads (ds_read_b128) and the V^T operand reads (ds_read_b64_tr_b16, a
+//     transposing read) spread over the LDS banks;
+//   * O is rescaled only when a row's running max grows by more than 2^8
+//     (exp2 units), otherwise the stale max is kept.
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -28,46 +34,53 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kRows = 128;  // query rows per workgroup
-constexpr int kBN = 64;     // keys per tile
-constexpr int kPadK = 8;    // bf16 padding per LDS row (bank spread)
-constexpr int kPadV = 8;
+constexpr int kRows = 128;     // query rows per workgroup
+constexpr int kBN = 64;        // keys per tile
+constexpr int kMaxBt = 1024;   // prefix block ids staged in LDS
+constexpr float kRescaleLog2 = 8.f;
 
 __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Position of key k (0..63) inside a V^T row: bits 2 and 3 swapped.
-__device__ __forceinline__ int vt_pos(int k) {
-  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+// Chunk swizzle of a K/V row inside a tile: 16-byte chunk c of row r is stored
+// at chunk position c ^ swz(r).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (r >> 1) & 7;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{lo, hi}, bf16x2_t));
 }
 
 template <int D>
-struct TileRegs {
-  static constexpr int KCH = kBN * D / 8 / 256;       // 16-byte K chunks per thread
-  static constexpr int VIT = (kBN / 2) * D / 8 / 256;  // (key pair, 8 dims) items per thread
-  u32x4 k[KCH];
-  u32x4 v0[VIT], v1[VIT];
-};
+__global__ __launch_bounds__(256, 2) void paged_prefill_kernel(PrefillArgs a, int tt_tokens,
+                                                            int ntt) {
+  constexpr int KS = D / 16;                    // 16-wide K steps over head_dim
+  constexpr int DT = D / 32;                    // 32-row tiles of O^T
+  constexpr int CPR = D / 8;                    // 16-byte chunks per K/V row
+  constexpr int RPI = 64 / CPR;                 // rows per 1 KiB direct-to-LDS load
+  constexpr int IPW = kBN / RPI / 4;            // such loads per wave per tile and tensor
+  constexpr int TILE = kBN * D;                 // elements of one K or V tile
 
-template <int D>
-__global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillArgs a, int tt_tokens,
-                                                               int ntt) {
-  constexpr int KS = D / 16;  // 16-wide K steps over head_dim
-  constexpr int DT = D / 32;  // 32-row tiles of O^T
-  constexpr int LPR = D / 8;  // 16-byte chunks per K/V row
-  using Regs = TileRegs<D>;
-
-  __shared__ __align__(16) uint16_t sK[kBN][D + kPadK];
-  __shared__ __align__(16) uint16_t sVt[D][kBN + kPadV];
+  extern __shared__ __align__(16) uint16_t smem[];
+  uint16_t* tiles = smem;                                   // [2 buffers][K, V][TILE]
+  int* s_bt = (int*)(smem + 4 * TILE);                      // prefix block ids
+  int* s_flags = s_bt + kMaxBt;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int lane = tid & 63;
   const int lr = lane & 31;  // this lane's query row within the wave
-  const int hi = lane >> 5;  // which half of the 16-wide K step
+  const int hi = lane >> 5;  // which half of a 16-wide K step
 
   // Heaviest token tiles first (later tiles attend to more keys).  The token
   // tiles of one (sequence, KV head) are B * Hkv workgroups apart, so they
@@ -82,9 +95,8 @@ __global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillArgs a, int t
   const int n = a.cu_seqlens_q[seq + 1] - qa;
   const int t0 = tt * tt_tokens;
   if (n <= 0 || t0 >= n) return;
-  int ctx = a.context_lens[seq];
   const int cap = a.mbs << a.bs_log2;
-  int P = ctx - n;
+  int P = a.context_lens[seq] - n;
   P = P < 0 ? 0 : (P > cap ? cap : P);
   const int t_hi = min(t0 + tt_tokens, n);
   const int kend = P + t_hi;  // keys this workgroup needs: 0 .. kend-1
@@ -102,127 +114,131 @@ __global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillArgs a, int t
 
   u32x4 qb[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
+  for (int ks = 0; ks < KS; ++ks)
     qb[ks] = row_ok ? *(const u32x4*)(a.q + qrow + ks * 16 + hi * 8) : u32x4{0u, 0u, 0u, 0u};
+
+  // Stage the prefix's block ids (invalid ids become -1).
+  const int nblk = (P + (1 << a.bs_log2) - 1) >> a.bs_log2;
+  const bool bt_in_lds = nblk <= kMaxBt;
+  if (tid == 0) s_flags[0] = 0;
+  __syncthreads();
+  if (bt_in_lds) {
+    bool bad = false;
+    for (int i = tid; i < nblk; i += blockDim.x) {
+      const int b = a.block_tables[(int64_t)seq * a.mbs + i];
+      const bool ok = b >= 0 && b < a.num_blocks;
+      s_bt[i] = ok ? b : -1;
+      bad |= !ok;
+    }
+    if (bad) s_flags[0] = 1;
   }
+  __syncthreads();
+  const bool has_bad = bt_in_lds ? s_flags[0] != 0 : true;
 
   const int bs_mask = (1 << a.bs_log2) - 1;
   const int64_t kv_stride = (int64_t)a.Hkv * D;
-
-  // Source of key kk: the paged cache below P, k_new / v_new from P on.
-  // Returns false (and a safe offset) for keys past kend or in an invalid block.
-  auto key_src = [&](int kk, int dchunk, int64_t& off, bool& from_new) -> bool {
-    from_new = kk >= P;
-    off = 0;
-    if (kk >= kend) return false;
-    if (from_new) {
-      off = (int64_t)(qa + kk - P) * kv_stride + kvh * D + dchunk * 8;
-      return true;
-    }
-    const int blk = a.block_tables[(int64_t)seq * a.mbs + (kk >> a.bs_log2)];
-    if (blk < 0 || blk >= a.num_blocks) return false;
-    off = (((int64_t)blk << a.bs_log2) + (kk & bs_mask)) * kv_stride + kvh * D + dchunk * 8;
-    return true;
-  };
-  auto load16 = [&](const uint16_t* cache, const uint16_t* fresh, int kk, int dchunk) -> u32x4 {
-    int64_t off;
-    bool from_new;
-    const bool ok = key_src(kk, dchunk, off, from_new);
-    const uint16_t* base = from_new ? fresh : cache;
-    const u32x4 v = *(const u32x4*)(base + off);
-    return ok ? v : u32x4{0u, 0u, 0u, 0u};
+  const int64_t head_off = (int64_t)kvh * D;
+  auto block_of = [&](int kk) -> int {
+    if (bt_in_lds) return s_bt[kk >> a.bs_log2];
+    const int b = a.block_tables[(int64_t)seq * a.mbs + (kk >> a.bs_log2)];
+    return (b >= 0 && b < a.num_blocks) ? b : -1;
   };
 
-  auto load_tile = [&](int j, Regs& rg) {
-    const int k0 = j * kBN;
+  // Issue the direct-to-LDS loads of tile j into buffer (j & 1).  Lane L of a
+  // load writes LDS chunk L of a 1 KiB run: row (inst * RPI + L / CPR), chunk
+  // position L % CPR, so it fetches global chunk (position ^ swz(row)).  Keys
+  // past kend or in an invalid block fetch the first new token's row (always
+  // valid, finite); the softmax masks them.
+  auto issue_tile = [&](int j) {
+    uint16_t* kdst = tiles + (j & 1) * 2 * TILE;
+    uint16_t* vdst = kdst + TILE;
 #pragma unroll
-    for (int i = 0; i < Regs::KCH; ++i) {
-      const int c = tid + 256 * i;
-      rg.k[i] = load16(a.k_cache, a.k_new, k0 + c / LPR, c % LPR);
-    }
-#pragma unroll
-    for (int i = 0; i < Regs::VIT; ++i) {
-      const int c = tid + 256 * i;
-      const int kp = c % (kBN / 2);
-      const int dchunk = c / (kBN / 2);
-      rg.v0[i] = load16(a.v_cache, a.v_new, k0 + 2 * kp, dchunk);
-      rg.v1[i] = load16(a.v_cache, a.v_new, k0 + 2 * kp + 1, dchunk);
-    }
-  };
-
-  auto store_tile = [&](const Regs& rg) {
-#pragma unroll
-    for (int i = 0; i < Regs::KCH; ++i) {
-      const int c = tid + 256 * i;
-      *(u32x4*)&sK[c / LPR][(c % LPR) * 8] = rg.k[i];
-    }
-#pragma unroll
-    for (int i = 0; i < Regs::VIT; ++i) {
-      const int c = tid + 256 * i;
-      const int kp = c % (kBN / 2);
-      const int d0 = (c / (kBN / 2)) * 8;
-      const int col = vt_pos(2 * kp);
-      const uint32_t x[4] = {rg.v0[i].x, rg.v0[i].y, rg.v0[i].z, rg.v0[i].w};
-      const uint32_t y[4] = {rg.v1[i].x, rg.v1[i].y, rg.v1[i].z, rg.v1[i].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // dims d0+2e and d0+2e+1: (key 2kp, key 2kp+1) pairs
-        *(uint32_t*)&sVt[d0 + 2 * e][col] = __builtin_amdgcn_perm(y[e], x[e], 0x05040100u);
-        *(uint32_t*)&sVt[d0 + 2 * e + 1][col] = __builtin_amdgcn_perm(y[e], x[e], 0x07060302u);
+    for (int i = 0; i < IPW; ++i) {
+      const int inst = w * IPW + i;
+      const int r = inst * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ swz<D>(r);
+      const int kk = j * kBN + r;
+      int64_t off = (int64_t)qa * kv_stride + head_off;
+      bool fresh = true;
+      if (kk < P) {
+        const int b = block_of(kk);
+        if (b >= 0) {
+          off = (((int64_t)b << a.bs_log2) + (kk & bs_mask)) * kv_stride + head_off;
+          fresh = false;
+        }
+      } else if (kk < kend) {
+        off = (int64_t)(qa + kk - P) * kv_stride + head_off;
       }
+      off += c * 8;
+      const uint16_t* ks = (fresh ? a.k_new : a.k_cache) + off;
+      const uint16_t* vs = (fresh ? a.v_new : a.v_cache) + off;
+      __builtin_amdgcn_global_load_lds(ks, (__attribute__((address_space(3))) void*)(kdst + inst * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vs, (__attribute__((address_space(3))) void*)(vdst + inst * 512), 16, 0, 0);
     }
   };
 
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
-  float m_run = kNegBig;  // running max of raw scores for this lane's row
-  float l_run = 0.f;      // this lane's share of the softmax denominator
+  f32x16 lacc = f32x16{};
+  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0
+  float m_run = kNegBig;  // running max (raw score units) of this lane's row
   const float c = a.scale_log2e;
 
-  Regs rg;
-  load_tile(0, rg);
+  issue_tile(0);
   for (int j = 0; j < ntiles; ++j) {
-    __syncthreads();  // every wave is done reading the previous tile
-    store_tile(rg);
-    __syncthreads();
-    if (j + 1 < ntiles) load_tile(j + 1, rg);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile j are in LDS
+    __syncthreads();                     // ... and every wave's; buffer (j+1)&1 is free again
+    if (j + 1 < ntiles) issue_tile(j + 1);
+    const uint16_t* sk = tiles + (j & 1) * 2 * TILE;
+    const uint16_t* sv = sk + TILE;
 
     // S^T = K Q^T for the two 32-key halves of the tile.
     f32x16 sacc[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       sacc[kt] = f32x16{};
+      const int r = kt * 32 + lr;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 ka = *(const u32x4*)&sK[kt * 32 + lr][ks * 16 + hi * 8];
+        const int p = (2 * ks + hi) ^ swz<D>(r);
+        const u32x4 ka = *(const u32x4*)(sk + r * D + p * 8);
         sacc[kt] = mfma32(ka, qb[ks], sacc[kt]);
       }
     }
-    // Causal / range mask: key k0 + key_local is visible to this row iff <= pos.
+    // Mask keys past this row's position (and keys of invalid blocks).
     const int k0 = j * kBN;
-    const bool need_mask = k0 + kBN - 1 > P + t0;  // some row of the workgroup may not see all keys
+    if (k0 + kBN - 1 > P + t0 || has_bad) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kk = k0 + kt * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
+          bool ok = kk <= pos;
+          if (has_bad && kk < P) ok = ok && block_of(kk) >= 0;
+          sacc[kt][i] = ok ? sacc[kt][i] : -INFINITY;
+        }
+      }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float sv = sacc[kt][i];
-        if (need_mask) {
-          const int kk = k0 + kt * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-          sv = kk <= pos ? sv : -INFINITY;
-        }
-        sacc[kt][i] = sv;
-        mx = fmaxf(mx, sv);
-      }
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
     }
     mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-    m_run = m_new;
-    const float mc = m_new * c;
+    // Lazy rescale: keep the stale max unless it grew by more than 2^8.
+    const bool grow = (mx - m_run) * c > kRescaleLog2;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      m_run = m_new;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+      lacc *= alpha;
+    }
+    const float mc = m_run * c;
     u32x4 pb[4];  // P^T operands of the four 16-key steps, bf16
-    float psum = 0.f;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       uint32_t wv[4];
@@ -230,30 +246,41 @@ __global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillArgs a, int t
       for (int e = 0; e < 4; ++e) {
         const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][(s & 1) * 8 + 2 * e], c, -mc));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][(s & 1) * 8 + 2 * e + 1], c, -mc));
-        const uint32_t b0 = f32_to_bf16_rne(p0);
-        const uint32_t b1 = f32_to_bf16_rne(p1);
-        psum += __uint_as_float(b0 << 16) + __uint_as_float(b1 << 16);  // sum of what the MFMA sees
-        wv[e] = b0 | (b1 << 16);
+        wv[e] = pack_bf16(p0, p1);
       }
       pb[s] = u32x4{wv[0], wv[1], wv[2], wv[3]};
     }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T and l += 1^T P^T.  The V^T operand of lane l is column
+    // d = 32 dt + (l & 31) at keys 16 s + {4 hi .. 4 hi + 3, 8 + 4 hi .. 8 + 4 hi + 3},
+    // gathered by two transposing reads: source lane i of a 16-lane group reads
+    // row (kb + i / 4), columns dbase + 4 (i % 4) .. + 3.
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const u32x4 va = *(const u32x4*)&sVt[dt * 32 + lr][s * 16 + hi * 8];
+        const int i16 = lane & 15;
+        const int dcol = dt * 32 + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
+        short4_t part[2];
+#pragma unroll
+        for (int rd = 0; rd < 2; ++rd) {
+          const int r = s * 16 + 4 * hi + 8 * rd + (i16 >> 2);
+          const int p = (dcol >> 3) ^ swz<D>(r);
+          const uint16_t* src = sv + r * D + p * 8 + (dcol & 7);
+          part[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (short4_t __attribute__((address_space(3)))*)src);
+        }
+        const u32x4 va = __builtin_bit_cast(u32x4, short8_t{part[0][0], part[0][1], part[0][2],
+                                                            part[0][3], part[1][0], part[1][1],
+                                                            part[1][2], part[1][3]});
         oacc[dt] = mfma32(va, pb[s], oacc[dt]);
       }
+      lacc = mfma32(ones, pb[s], lacc);
     }
   }
 
-  const float l_tot = l_run + shfl_xor(l_run, 32);
   if (!row_ok) return;
+  const float l_tot = lacc[0];
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
@@ -265,12 +292,35 @@ __global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillArgs a, int t
       if (a.out_f32) {
         *(float4*)((float*)a.out + qrow + d) = make_float4(o0, o1, o2, o3);
       } else {
-        const uint32_t w0 = f32_to_bf16_rne(o0) | (f32_to_bf16_rne(o1) << 16);
-        const uint32_t w1 = f32_to_bf16_rne(o2) | (f32_to_bf16_rne(o3) << 16);
-        *(uint2*)((uint16_t*)a.out + qrow + d) = make_uint2(w0, w1);
+        *(uint2*)((uint16_t*)a.out + qrow + d) = make_uint2(pack_bf16(o0, o1), pack_bf16(o2, o3));
       }
     }
   }
+}
+
+template <int D>
+constexpr size_t prefill_smem_bytes() {
+  return (size_t)4 * kBN * D * sizeof(uint16_t) + (kMaxBt + 4) * sizeof(int);
+}
+
+template <int D>
+int launch_prefill_d(const PrefillArgs& a, int tt_tokens, int ntt, int64_t nwg,
+                     hipStream_t stream) {
+  constexpr size_t smem = prefill_smem_bytes<D>();
+  // More than 64 KiB of dynamic LDS must be allowed once per device.
+  static std::atomic<uint64_t> configured{0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (!(configured.load() & bit)) {
+    if (hipFuncSetAttribute((const void*)paged_prefill_kernel<D>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
+      return -1;
+    configured.fetch_or(bit);
+  }
+  hipLaunchKernelGGL(paged_prefill_kernel<D>, dim3((unsigned)nwg), dim3(256), smem, stream, a,
+                     tt_tokens, ntt);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 }  // namespace
@@ -282,16 +332,9 @@ int launch_paged_prefill(const PrefillArgs& a, int head_dim, hipStream_t stream)
   const int64_t nwg = (int64_t)ntt * a.B * a.Hkv;
   if (nwg == 0) return 0;
   if (nwg > INT32_MAX) return -2;
-  if (head_dim == 128) {
-    hipLaunchKernelGGL(paged_prefill_kernel<128>, dim3((unsigned)nwg), dim3(256), 0, stream, a,
-                       tt_tokens, ntt);
-  } else if (head_dim == 64) {
-    hipLaunchKernelGGL(paged_prefill_kernel<64>, dim3((unsigned)nwg), dim3(256), 0, stream, a,
-                       tt_tokens, ntt);
-  } else {
-    return -3;
-  }
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+  if (head_dim == 128) return launch_prefill_d<128>(a, tt_tokens, ntt, nwg, stream);
+  if (head_dim == 64) return launch_prefill_d<64>(a, tt_tokens, ntt, nwg, stream);
+  return -3;
 }
 
 }  // namespace pa

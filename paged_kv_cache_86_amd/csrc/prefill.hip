@@ -138,26 +138,72 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_kernel(PrefillArgs a, in
   const int bs_mask = (1 << a.bs_log2) - 1;
   const int64_t kv_stride = (int64_t)a.Hkv * D;
   const int64_t head_off = (int64_t)kvh * D;
-  auto block_of = [&](int kk) -> int {
+  auto block_of = [&](int kk) __device__ -> int {
     if (bt_in_lds) return s_bt[kk >> a.bs_log2];
     const int b = a.block_tables[(int64_t)seq * a.mbs + (kk >> a.bs_log2)];
     return (b >= 0 && b < a.num_blocks) ? b : -1;
   };
 
-  // Issue the direct-to-LDS loads of tile j into buffer (j & 1).  Lane L of a
-  // load writes LDS chunk L of a 1 KiB run: row (inst * RPI + L / CPR), chunk
-  // position L % CPR, so it fetches global chunk (position ^ swz(row)).  Keys
-  // past kend or in an invalid block fetch the first new token's row (always
-  // valid, finite); the softmax masks them.
-  auto issue_tile = [&](int j) {
-    uint16_t* kdst = tiles + (j & 1) * 2 * TILE;
-    uint16_t* vdst = kdst + TILE;
+  // Byte offsets inside the tile area.  A buffer holds the K tile then the V
+  // tile (TILE elements each); buffer 1 follows buffer 0.
+  constexpr int TB = TILE * 2;         // bytes of one K or V tile
+  constexpr int BUFB = 2 * TB;         // bytes of one buffer
+  const char* lds = (const char*)tiles;
+
+  // Loader: lane L of load `i` of this wave fills LDS chunk L of row
+  // r_i = inst * RPI + L / CPR with global chunk (L % CPR) ^ swz(r_i).  The
+  // lane's element offset inside a source row run is loop-invariant.
+  int lrow[IPW];
+  int lpart[IPW];  // (r_i * kv_stride + chunk * 8) in elements
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int inst = w * IPW + i;
+    lrow[i] = inst * RPI + lane / CPR;
+    lpart[i] = lrow[i] * (int)kv_stride + (((lane % CPR) ^ swz<D>(lrow[i])) * 8);
+  }
+  const int bsz = 1 << a.bs_log2;
+
+  // Issue the direct-to-LDS loads of tile j.  Uniform fast paths: a tile that
+  // lies inside one cache block, or wholly among the new tokens, has one base
+  // address plus the lane's fixed offset.  Otherwise each lane resolves its
+  // own key; keys past kend or in an invalid block fetch the first new token's
+  // row (valid, finite) and the softmax masks them.
+  auto issue_tile = [&](int j, int buf) __device__ {
+    char* kdst = (char*)tiles + buf * BUFB;
+    char* vdst = kdst + TB;
+    const int k0 = j * kBN;
+    const uint16_t* kbase = nullptr;
+    const uint16_t* vbase = nullptr;
+    if (k0 + kBN <= P && bsz >= kBN) {
+      const int b = block_of(k0);
+      if (b >= 0) {
+        const int64_t o = (((int64_t)b << a.bs_log2) + (k0 & bs_mask)) * kv_stride + head_off;
+        kbase = a.k_cache + o;
+        vbase = a.v_cache + o;
+      }
+    } else if (k0 >= P && k0 + kBN <= kend) {
+      const int64_t o = (int64_t)(qa + k0 - P) * kv_stride + head_off;
+      kbase = a.k_new + o;
+      vbase = a.v_new + o;
+    }
+    if (kbase != nullptr) {
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const int inst = w * IPW + i;
+        // (named pointers: an arithmetic expression as the builtin's argument
+        // makes the host pass silently drop the kernel's launch stub)
+        const uint16_t* kp = kbase + lpart[i];
+        const uint16_t* vp = vbase + lpart[i];
+        __builtin_amdgcn_global_load_lds(kp, (__attribute__((address_space(3))) void*)(kdst + inst * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vp, (__attribute__((address_space(3))) void*)(vdst + inst * 1024), 16, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int inst = w * IPW + i;
-      const int r = inst * RPI + lane / CPR;
-      const int c = (lane % CPR) ^ swz<D>(r);
-      const int kk = j * kBN + r;
+      const int r = lrow[i];
+      const int kk = k0 + r;
       int64_t off = (int64_t)qa * kv_stride + head_off;
       bool fresh = true;
       if (kk < P) {
@@ -169,13 +215,38 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_kernel(PrefillArgs a, in
       } else if (kk < kend) {
         off = (int64_t)(qa + kk - P) * kv_stride + head_off;
       }
-      off += c * 8;
+      off += lpart[i] - r * (int)kv_stride;  // the lane's chunk within the row
       const uint16_t* ks = (fresh ? a.k_new : a.k_cache) + off;
       const uint16_t* vs = (fresh ? a.v_new : a.v_cache) + off;
-      __builtin_amdgcn_global_load_lds(ks, (__attribute__((address_space(3))) void*)(kdst + inst * 512), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vs, (__attribute__((address_space(3))) void*)(vdst + inst * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(ks, (__attribute__((address_space(3))) void*)(kdst + inst * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vs, (__attribute__((address_space(3))) void*)(vdst + inst * 1024), 16, 0, 0);
     }
   };
+
+  // Operand read offsets.  K operand of (kt, ks): row 32 kt + lr, chunk
+  // 2 ks + hi; V^T operand of (s, dt, rd): row 16 s + 4 hi + 8 rd + i16 / 4,
+  // element 32 dt + 16 ((lane >> 4) & 1) + 4 (i16 & 3).  The swizzle only
+  // depends on the row modulo 16, which kt and s do not change, so every
+  // offset is a per-lane base (computed once here) plus a constant.
+  int kofs[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int r = lr;
+    kofs[ks] = r * D * 2 + (((2 * ks + hi) ^ swz<D>(r)) * 16);
+  }
+  int vofs[DT][2];
+  {
+    const int i16 = lane & 15;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int rd = 0; rd < 2; ++rd) {
+        const int r = 4 * hi + 8 * rd + (i16 >> 2);
+        const int dcol = dt * 32 + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
+        vofs[dt][rd] = TB + r * D * 2 + (((dcol >> 3) ^ swz<D>(r)) * 16) + (dcol & 7) * 2;
+      }
+    }
+  }
 
   f32x16 oacc[DT];
 #pragma unroll
@@ -185,24 +256,14 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_kernel(PrefillArgs a, in
   float m_run = kNegBig;  // running max (raw score units) of this lane's row
   const float c = a.scale_log2e;
 
-  issue_tile(0);
-  for (int j = 0; j < ntiles; ++j) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile j are in LDS
-    __syncthreads();                     // ... and every wave's; buffer (j+1)&1 is free again
-    if (j + 1 < ntiles) issue_tile(j + 1);
-    const uint16_t* sk = tiles + (j & 1) * 2 * TILE;
-    const uint16_t* sv = sk + TILE;
-
+  auto compute_tile = [&](int j, int bufoff) __device__ {
     // S^T = K Q^T for the two 32-key halves of the tile.
-    f32x16 sacc[2];
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      sacc[kt] = f32x16{};
-      const int r = kt * 32 + lr;
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int p = (2 * ks + hi) ^ swz<D>(r);
-        const u32x4 ka = *(const u32x4*)(sk + r * D + p * 8);
+      for (int kt = 0; kt < 2; ++kt) {
+        const u32x4 ka = *(const u32x4*)(lds + bufoff + kofs[ks] + kt * 32 * D * 2);
         sacc[kt] = mfma32(ka, qb[ks], sacc[kt]);
       }
     }
@@ -240,42 +301,55 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_kernel(PrefillArgs a, in
     const float mc = m_run * c;
     u32x4 pb[4];  // P^T operands of the four 16-key steps, bf16
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s4 = 0; s4 < 4; ++s4) {
       uint32_t wv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][(s & 1) * 8 + 2 * e], c, -mc));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][(s & 1) * 8 + 2 * e + 1], c, -mc));
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[s4 >> 1][(s4 & 1) * 8 + 2 * e], c, -mc));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[s4 >> 1][(s4 & 1) * 8 + 2 * e + 1], c, -mc));
         wv[e] = pack_bf16(p0, p1);
       }
-      pb[s] = u32x4{wv[0], wv[1], wv[2], wv[3]};
+      pb[s4] = u32x4{wv[0], wv[1], wv[2], wv[3]};
     }
-
     // O^T += V^T P^T and l += 1^T P^T.  The V^T operand of lane l is column
-    // d = 32 dt + (l & 31) at keys 16 s + {4 hi .. 4 hi + 3, 8 + 4 hi .. 8 + 4 hi + 3},
+    // 32 dt + (l & 31) at keys 16 s + {4 hi .. 4 hi + 3, 8 + 4 hi .. 8 + 4 hi + 3},
     // gathered by two transposing reads: source lane i of a 16-lane group reads
-    // row (kb + i / 4), columns dbase + 4 (i % 4) .. + 3.
+    // row (kb + i / 4), elements dbase + 4 (i % 4) .. + 3.
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s4 = 0; s4 < 4; ++s4) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const int i16 = lane & 15;
-        const int dcol = dt * 32 + 16 * ((lane >> 4) & 1) + 4 * (i16 & 3);
         short4_t part[2];
 #pragma unroll
         for (int rd = 0; rd < 2; ++rd) {
-          const int r = s * 16 + 4 * hi + 8 * rd + (i16 >> 2);
-          const int p = (dcol >> 3) ^ swz<D>(r);
-          const uint16_t* src = sv + r * D + p * 8 + (dcol & 7);
+          const char* src = lds + bufoff + vofs[dt][rd] + s4 * 16 * D * 2;
           part[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (short4_t __attribute__((address_space(3)))*)src);
         }
         const u32x4 va = __builtin_bit_cast(u32x4, short8_t{part[0][0], part[0][1], part[0][2],
                                                             part[0][3], part[1][0], part[1][1],
                                                             part[1][2], part[1][3]});
-        oacc[dt] = mfma32(va, pb[s], oacc[dt]);
+        oacc[dt] = mfma32(va, pb[s4], oacc[dt]);
       }
-      lacc = mfma32(ones, pb[s], lacc);
+      lacc = mfma32(ones, pb[s4], lacc);
+    }
+  };
+
+  // The operand offsets point into buffer (j & 1): flipping the buffer bit of
+  // every offset after each tile keeps the reads at "register + constant".
+  // BUFB is a power of two larger than every in-buffer offset.
+  issue_tile(0, 0);
+  for (int j = 0; j < ntiles; ++j) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile j are in LDS
+    __syncthreads();                     // ... and every wave's; the other buffer is free again
+    if (j + 1 < ntiles) issue_tile(j + 1, (j + 1) & 1);
+    compute_tile(j, 0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kofs[ks] ^= BUFB;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      vofs[dt][0] ^= BUFB;
+      vofs[dt][1] ^= BUFB;
     }
   }
 

@@ -10,21 +10,40 @@
 
 namespace pa {
 
-// One thread moves 16 bytes (8 bf16) of K or V; blockIdx.y selects K (0) or V (1).
+// Each thread moves kStoreItems 16-byte vectors (8 bf16 each) of K and the
+// same vectors of V: all loads are issued before the first store.  Vector e
+// of token t is element (t * row_vecs + e) of the flat [T * row_vecs] view;
+// its destination is row slot_mapping[t] of the [NB * BS, row_vecs] cache.
+constexpr int kStoreItems = 4;
+
 __global__ __launch_bounds__(256) void kvcache_store_kernel(
     const u32x4* __restrict__ k, const u32x4* __restrict__ v,
     const int32_t* __restrict__ slot_mapping, u32x4* __restrict__ k_cache,
     u32x4* __restrict__ v_cache, int T, int row_vecs, int64_t num_slots) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = (int64_t)T * row_vecs;
-  if (idx >= total) return;
-  const int t = (int)(idx / row_vecs);
-  const int e = (int)(idx - (int64_t)t * row_vecs);
-  const int32_t s = slot_mapping[t];
-  if (s < 0 || (int64_t)s >= num_slots) return;
-  const u32x4* src = blockIdx.y == 0 ? k : v;
-  u32x4* dst = blockIdx.y == 0 ? k_cache : v_cache;
-  dst[(int64_t)s * row_vecs + e] = src[(int64_t)t * row_vecs + e];
+  const int64_t first = (int64_t)blockIdx.x * 256 * kStoreItems + threadIdx.x;
+  u32x4 kv[kStoreItems], vv[kStoreItems];
+  int64_t dst[kStoreItems];
+#pragma unroll
+  for (int i = 0; i < kStoreItems; ++i) {
+    const int64_t idx = first + (int64_t)i * 256;
+    dst[i] = -1;
+    if (idx < total) {
+      const int t = (int)(idx / row_vecs);
+      const int e = (int)(idx - (int64_t)t * row_vecs);
+      const int32_t s = slot_mapping[t];
+      kv[i] = k[idx];
+      vv[i] = v[idx];
+      if (s >= 0 && (int64_t)s < num_slots) dst[i] = (int64_t)s * row_vecs + e;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kStoreItems; ++i) {
+    if (dst[i] >= 0) {
+      k_cache[dst[i]] = kv[i];
+      v_cache[dst[i]] = vv[i];
+    }
+  }
 }
 
 int launch_kvcache_store(const void* k, const void* v, const int32_t* slot_mapping, int T,
@@ -33,7 +52,8 @@ int launch_kvcache_store(const void* k, const void* v, const int32_t* slot_mappi
   if (T == 0) return 0;
   const int row_vecs = num_kv_heads * head_dim / 8;
   const int64_t total = (int64_t)T * row_vecs;
-  dim3 grid((unsigned)((total + 255) / 256), 2);
+  const int64_t per_wg = 256 * kStoreItems;
+  dim3 grid((unsigned)((total + per_wg - 1) / per_wg));
   hipLaunchKernelGGL(kvcache_store_kernel, grid, dim3(256), 0, stream,
                      (const u32x4*)k, (const u32x4*)v, slot_mapping, (u32x4*)k_cache,
                      (u32x4*)v_cache, T, row_vecs, (int64_t)num_blocks * block_size);

@@ -11,6 +11,15 @@ Every function is pinned by ``tests/test_oracle.py`` (closed forms, brute
 force on tiny inputs, a library attention routine, permutation invariance and
 the pages' worked examples); there is no "parity unpinned" function here.
 """
+from .fp8 import (  # noqa: F401
+    E4M3_MAX,
+    dequantize,
+    e4m3_decode,
+    e4m3_encode,
+    kvcache_store_fp8,
+    paged_decode_fp8,
+    quantize,
+)
 from .paged_attention import (  # noqa: F401
     bf16_to_f64,
     kv_head_for,

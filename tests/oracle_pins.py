@@ -346,4 +346,97 @@ def pin_prefill_is_causal():
     assert not np.array_equal(out[6:], out2[6:])
 
 
+
+
+# --------------------------------------------------------------------------- FP8 KV cache
+
+def pin_e4m3_known_codes():
+    """Values fixed by the OCP FP8 E4M3 format."""
+    from oracle import e4m3_decode
+    want = {0x38: 1.0, 0x7E: 448.0, 0x01: 2.0 ** -9, 0x08: 2.0 ** -6, 0x07: 7 * 2.0 ** -9,
+            0xBC: -1.5, 0x40: 2.0, 0x3F: 1.875, 0x00: 0.0, 0x5A: 20.0}
+    for code, val in want.items():
+        assert e4m3_decode([code])[0] == val, hex(code)
+    assert np.isnan(e4m3_decode([0x7F])[0]) and np.isnan(e4m3_decode([0xFF])[0])
+    assert np.signbit(e4m3_decode([0x80])[0]) and e4m3_decode([0x80])[0] == 0.0
+
+
+def pin_e4m3_round_trip():
+    from oracle import e4m3_decode, e4m3_encode
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    assert np.array_equal(e4m3_encode(e4m3_decode(codes)), codes)
+
+
+def pin_e4m3_matches_torch_in_range():
+    """torch's float8_e4m3fn cast (round to nearest even) on in-range values, midpoints included."""
+    from oracle import e4m3_decode, e4m3_encode
+    vals = e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = 0.5 * (vals[:-1] + vals[1:])
+    rng = np.random.default_rng(30)
+    x = np.concatenate([mids, -mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9),
+                        rng.uniform(-448, 448, 4000), rng.standard_normal(4000) * 0.01]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(e4m3_encode(x.astype(np.float64)), ref)
+
+
+def pin_e4m3_saturates():
+    from oracle import e4m3_encode
+    got = e4m3_encode(np.array([448.0, 463.9, 464.0, 480.0, 1e6, np.inf, -1e9, -np.inf]))
+    assert got.tolist() == [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE]
+    assert (e4m3_encode(np.array([np.nan]))[0] & 0x7F) == 0x7F
+
+
+def pin_fp8_quantize_power_of_two_scale():
+    """Dividing by 2^k before rounding equals rounding the exponent-shifted value."""
+    from oracle import e4m3_encode, quantize
+    rng = np.random.default_rng(31)
+    bits = _bits(rng.standard_normal(3000) * 40)
+    x = oracle.bf16_to_f64(bits)
+    for k in (-3, 0, 2):
+        assert np.array_equal(quantize(bits, 2.0 ** k), e4m3_encode(x / 2.0 ** k))
+
+
+def pin_fp8_decode_reduces_to_bf16_decode():
+    """With values exactly representable in E4M3 and scales 1, FP8 decode equals the bf16 decode."""
+    from oracle import paged_decode_fp8
+    c = decode_case(32, [40, 7, 100], 4, 2, 64, 16, nb_factor=1.5)
+    rng = np.random.default_rng(33)
+    codes_k = rng.integers(0, 0x7F, size=c.k_cache.shape).astype(np.uint8) | (
+        rng.integers(0, 2, size=c.k_cache.shape).astype(np.uint8) << 7)
+    codes_v = rng.integers(0, 0x7F, size=c.v_cache.shape).astype(np.uint8)
+    codes_k[(codes_k & 0x7F) == 0x7F] = 0x38
+    vals_k = oracle.e4m3_decode(codes_k).astype(np.float32)
+    vals_v = oracle.e4m3_decode(codes_v).astype(np.float32)
+    bits_k = (vals_k.view(np.uint32) >> 16).astype(np.uint16)  # exact: E4M3 fits in bf16
+    bits_v = (vals_v.view(np.uint32) >> 16).astype(np.uint16)
+    a = paged_decode_fp8(c.q, codes_k, codes_v, c.block_tables, c.context_lens, SCALE64, 1.0, 1.0)
+    b = oracle.paged_decode(c.q, bits_k, bits_v, c.block_tables, c.context_lens, SCALE64)
+    assert np.array_equal(a, b)
+    # scales multiply K and V
+    a2 = paged_decode_fp8(c.q, codes_k, codes_v, c.block_tables, c.context_lens, SCALE64, 0.5, 4.0)
+    bits_k2 = ((vals_k * 0.5).view(np.uint32) >> 16).astype(np.uint16)
+    bits_v2 = ((vals_v * 4.0).view(np.uint32) >> 16).astype(np.uint16)
+    b2 = oracle.paged_decode(c.q, bits_k2, bits_v2, c.block_tables, c.context_lens, SCALE64)
+    assert np.max(np.abs(a2 - b2)) < 1e-12
+
+
+def pin_fp8_store_writes_exactly_mapped_slots():
+    from oracle import kvcache_store_fp8, quantize
+    rng = np.random.default_rng(34)
+    NB, BS, Hkv, D, T = 6, 8, 2, 64, 15
+    base = rng.integers(0, 256, size=(NB, BS, Hkv, D), dtype=np.uint8)
+    k = _bits(rng.standard_normal((T, Hkv, D)) * 3)
+    v = _bits(rng.standard_normal((T, Hkv, D)))
+    slots = rng.choice(NB * BS, size=T, replace=False).astype(np.int32)
+    slots[[2, 9]] = -1
+    kc, vc = kvcache_store_fp8(k, v, slots, base, base.copy(), 0.03, 0.5)
+    where = {int(s): t for t, s in enumerate(slots) if s >= 0}
+    kq, vq = quantize(k, 0.03), quantize(v, 0.5)
+    for b in range(NB):
+        for o in range(BS):
+            t = where.get(b * BS + o)
+            assert np.array_equal(kc[b, o], base[b, o] if t is None else kq[t])
+            assert np.array_equal(vc[b, o], base[b, o] if t is None else vq[t])
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

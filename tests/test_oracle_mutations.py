@@ -3,14 +3,15 @@ import numpy as np
 import pytest
 
 import oracle
+import oracle.fp8 as fp8_oracle
 import oracle.paged_attention as pa_oracle
 from oracle_pins import PINS
 
 
 def _caught(monkeypatch, name, replacement):
-    monkeypatch.setattr(pa_oracle, name, replacement)
-    if hasattr(oracle, name):
-        monkeypatch.setattr(oracle, name, replacement)
+    for mod in (pa_oracle, fp8_oracle, oracle):
+        if hasattr(mod, name):
+            monkeypatch.setattr(mod, name, replacement)
     failed = []
     for pin in PINS:
         try:
@@ -72,6 +73,27 @@ def _store_next_slot(k, v, slot_mapping, k_cache, v_cache):
 
 
 ORIGINAL_STORE = pa_oracle.kvcache_store
+ORIGINAL_ENCODE = fp8_oracle.e4m3_encode
+
+
+def _encode_ties_away(x):
+    x = np.asarray(x, dtype=np.float64)
+    nudged = x + np.sign(x) * np.abs(x) * 1e-12  # pushes exact ties upward in magnitude
+    return ORIGINAL_ENCODE(nudged)
+
+
+def _encode_no_saturation(x):
+    x = np.asarray(x, dtype=np.float64)
+    code = ORIGINAL_ENCODE(x)
+    return np.where(np.abs(x) > 448.0, np.uint8(0x7F) | (code & 0x80), code).astype(np.uint8)
+
+
+def _encode_truncate(x):
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    vals = fp8_oracle.E4M3_TABLE[:0x7F]
+    lo = np.clip(np.searchsorted(vals, np.minimum(a, 448.0), side="right") - 1, 0, 0x7E)
+    return (lo.astype(np.uint8) | (np.signbit(x).astype(np.uint8) << 7)).astype(np.uint8)
 
 MUTATIONS = {
     "gqa_modulo": ("kv_head_for", lambda h, g: h % max(1, g) if g > 1 else h // g),
@@ -85,6 +107,13 @@ MUTATIONS = {
     "unpage_swapped_axes": ("unpage", _unpage_swapped),
     "unpage_off_by_one": ("unpage", _unpage_offset_by_one),
     "store_next_slot": ("kvcache_store", _store_next_slot),
+    "e4m3_ties_away": ("e4m3_encode", _encode_ties_away),
+    "e4m3_no_saturation": ("e4m3_encode", _encode_no_saturation),
+    "e4m3_truncates": ("e4m3_encode", _encode_truncate),
+    "e4m3_bias_8": ("e4m3_decode", lambda c: fp8_oracle.E4M3_TABLE[np.asarray(c, np.uint8)] / 2.0),
+    "fp8_dequant_ignores_scale": ("dequantize", lambda c, s: fp8_oracle.e4m3_decode(c)),
+    "fp8_quant_multiplies": ("quantize", lambda b, s: fp8_oracle.e4m3_encode(
+        oracle.bf16_to_f64(b) * np.float32(s))),
     "bf16_shift_8": ("bf16_to_f64", lambda b: (np.asarray(b, np.uint16).astype(np.uint32) << 8)
                      .view(np.float32).astype(np.float64)),
 }

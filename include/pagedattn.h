@@ -11,7 +11,10 @@
  *   pa_paged_decode    one query token per sequence over its paged context
  *   pa_paged_prefill   a chunk of new tokens over a cached prefix plus itself, causal
  *
- * plus pa_paged_gather, a test aid that un-pages a cache through the block tables.
+ * plus pa_paged_gather, a test aid that un-pages a cache through the block tables,
+ * and the FP8 cache variants pa_kvcache_store_fp8 / pa_paged_decode_fp8 (VLLM
+ * 0.7.3 source article §5.3: the KV cache may be kept in FP8 while the
+ * attention output stays in high precision).
  *
  * Common conventions
  * ------------------
@@ -112,6 +115,48 @@ int pa_paged_decode(const void* q, const void* k_cache, const void* v_cache,
                     int num_kv_heads, int head_dim, int block_size, int num_blocks, float scale,
                     void* out, int out_dtype, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/*
+ * FP8 KV cache (VLLM 0.7.3 source article §5.3, KV cache precision: the cache
+ * is stored in FP8 while attention outputs stay in high precision).  The page
+ * fixes neither format nor scaling; this library uses OCP FP8 E4M3 codes
+ * (4 exponent bits, bias 7, 3 mantissa bits, subnormals, no infinities,
+ * NaN = S.1111.111, largest magnitude 448) with one fp32 scale per tensor:
+ * a value x is stored as E4M3(x / scale) and read back as decode(code) * scale.
+ * The pools have the bf16 layout with one byte per element:
+ * [num_blocks, block_size, num_kv_heads, head_dim] uint8.
+ *
+ * pa_kvcache_store_fp8: as pa_kvcache_store, but each bf16 element x of k (v)
+ * becomes the code nearest to x / k_scale (x / v_scale), the division in fp32
+ * (correctly rounded), the rounding to E4M3 to nearest with ties to the even
+ * code, magnitudes above 448 saturating to 448, NaN stored as NaN with its
+ * sign.  k_scale and v_scale must be finite and > 0 (else PA_ERR_SHAPE).
+ */
+int pa_kvcache_store_fp8(const void* k, const void* v, const int32_t* slot_mapping, int T,
+                         void* k_cache, void* v_cache, int num_blocks, int block_size,
+                         int num_kv_heads, int head_dim, float k_scale, float v_scale,
+                         void* stream);
+
+/* Workspace bytes for pa_paged_decode_fp8 (0 if the sizes are invalid). */
+size_t pa_paged_decode_fp8_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
+                                           int head_dim, int block_size,
+                                           int max_blocks_per_seq);
+
+/*
+ * pa_paged_decode on FP8 pools (layout above): attention over the
+ * dequantized keys decode(code) * k_scale and values decode(code) * v_scale;
+ * q and out as for pa_paged_decode.  The codes are widened exactly (K to
+ * bf16, V to fp32); k_scale is folded into the score scale and v_scale
+ * multiplies the merged outputs, so the only rounding beyond the bf16 path is
+ * that of the products.  k_scale and v_scale must be finite and > 0.
+ * Limits, workspace rules and determinism as for pa_paged_decode.
+ */
+int pa_paged_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, int max_blocks_per_seq,
+                        const int32_t* context_lens, int num_seqs, int num_q_heads,
+                        int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                        float scale, float k_scale, float v_scale, void* out, int out_dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Prefix-hit prefill ("Nano-vLLM源码学习(2)" §2: the prefix-hit prefill path

@@ -30,6 +30,9 @@ EXPORTED_SYMBOLS = (
     "pa_paged_decode",
     "pa_paged_prefill",
     "pa_paged_gather",
+    "pa_kvcache_store_fp8",
+    "pa_paged_decode_fp8_workspace_bytes",
+    "pa_paged_decode_fp8",
 )
 
 _lib = None
@@ -64,6 +67,13 @@ def load_library() -> ctypes.CDLL:
     lib.pa_paged_prefill.restype = I
     lib.pa_paged_gather.argtypes = [P, P, I, P, P, I, I, I, I, I, I, P, P]
     lib.pa_paged_gather.restype = I
+    lib.pa_kvcache_store_fp8.argtypes = [P, P, P, I, P, P, I, I, I, I, F, F, P]
+    lib.pa_kvcache_store_fp8.restype = I
+    lib.pa_paged_decode_fp8_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.pa_paged_decode_fp8_workspace_bytes.restype = Z
+    lib.pa_paged_decode_fp8.argtypes = [P, P, P, P, I, P, I, I, I, I, I, I, F, F, F, P, I, P, Z,
+                                        P]
+    lib.pa_paged_decode_fp8.restype = I
     _lib = lib
     return lib
 
@@ -113,10 +123,11 @@ def _out_dtype(out) -> int:
     raise TypeError(f"out must be bfloat16 or float32, got {out.dtype}")
 
 
-def _cache_geometry(k_cache, v_cache):
+def _cache_geometry(k_cache, v_cache, dtype=None):
     torch = _torch()
-    _check(k_cache, torch.bfloat16, "k_cache", 4)
-    _check(v_cache, torch.bfloat16, "v_cache", 4)
+    dtype = torch.bfloat16 if dtype is None else dtype
+    _check(k_cache, dtype, "k_cache", 4)
+    _check(v_cache, dtype, "v_cache", 4)
     if k_cache.shape != v_cache.shape:
         raise ValueError("k_cache and v_cache must have the same shape")
     return tuple(int(x) for x in k_cache.shape)  # NB, BS, Hkv, D
@@ -160,11 +171,8 @@ def decode_workspace(nbytes: int, device):
     return ws
 
 
-def paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale: Optional[float], out,
-                 workspace=None) -> None:
-    """out[i, h] = softmax(scale * q[i, h] . K_i^T) V_i over the paged context of sequence i."""
+def _decode_shapes(q, block_tables, context_lens, out, D):
     torch = _torch()
-    NB, BS, Hkv, D = _cache_geometry(k_cache, v_cache)
     _check(q, torch.bfloat16, "q", 3)
     _check(block_tables, torch.int32, "block_tables", 2)
     _check(context_lens, torch.int32, "context_lens", 1)
@@ -176,18 +184,70 @@ def paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale: Optiona
     _check(out, out.dtype, "out", 3)
     if tuple(out.shape) != (B, Hq, D):
         raise ValueError(f"out must be [{B}, {Hq}, {D}]")
-    MBS = int(block_tables.shape[1])
-    need = decode_workspace_bytes(B, Hq, Hkv, D, BS, MBS) if B > 0 else 0
+    return B, Hq, int(block_tables.shape[1])
+
+
+def _workspace_for(workspace, need, device):
     if workspace is None:
-        workspace = decode_workspace(need, q.device)
-    else:
-        _check(workspace, torch.uint8, "workspace", 1)
+        return decode_workspace(need, device)
+    _check(workspace, _torch().uint8, "workspace", 1)
+    return workspace
+
+
+def paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale: Optional[float], out,
+                 workspace=None) -> None:
+    """out[i, h] = softmax(scale * q[i, h] . K_i^T) V_i over the paged context of sequence i."""
+    NB, BS, Hkv, D = _cache_geometry(k_cache, v_cache)
+    B, Hq, MBS = _decode_shapes(q, block_tables, context_lens, out, D)
+    need = decode_workspace_bytes(B, Hq, Hkv, D, BS, MBS) if B > 0 else 0
+    workspace = _workspace_for(workspace, need, q.device)
     sc = float(scale) if scale is not None else 0.0
     rc = load_library().pa_paged_decode(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), MBS, _ptr(context_lens), B, Hq,
         Hkv, D, BS, NB, sc, _ptr(out), _out_dtype(out), _ptr(workspace), int(workspace.numel()),
         _stream(q.device))
     _raise_on("pa_paged_decode", rc)
+
+
+def kvcache_store_fp8(k, v, slot_mapping, k_cache, v_cache, k_scale: float,
+                      v_scale: float) -> None:
+    """Quantize row t of k/v to E4M3 codes (x / scale) into uint8 cache slot ``slot_mapping[t]``."""
+    torch = _torch()
+    NB, BS, Hkv, D = _cache_geometry(k_cache, v_cache, torch.uint8)
+    _check(k, torch.bfloat16, "k", 3)
+    _check(v, torch.bfloat16, "v", 3)
+    _check(slot_mapping, torch.int32, "slot_mapping", 1)
+    T = int(k.shape[0])
+    if tuple(k.shape) != (T, Hkv, D) or tuple(v.shape) != (T, Hkv, D):
+        raise ValueError(f"k and v must be [T, {Hkv}, {D}]")
+    if slot_mapping.shape[0] != T:
+        raise ValueError("slot_mapping must have one entry per token")
+    rc = load_library().pa_kvcache_store_fp8(
+        _ptr(k), _ptr(v), _ptr(slot_mapping), T, _ptr(k_cache), _ptr(v_cache), NB, BS, Hkv, D,
+        float(k_scale), float(v_scale), _stream(k.device))
+    _raise_on("pa_kvcache_store_fp8", rc)
+
+
+def decode_fp8_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                               head_dim: int, block_size: int, max_blocks_per_seq: int) -> int:
+    return int(load_library().pa_paged_decode_fp8_workspace_bytes(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq))
+
+
+def paged_decode_fp8(q, k_cache, v_cache, block_tables, context_lens, scale: Optional[float],
+                     k_scale: float, v_scale: float, out, workspace=None) -> None:
+    """Decode over uint8 E4M3 pools: keys code * k_scale, values code * v_scale."""
+    torch = _torch()
+    NB, BS, Hkv, D = _cache_geometry(k_cache, v_cache, torch.uint8)
+    B, Hq, MBS = _decode_shapes(q, block_tables, context_lens, out, D)
+    need = decode_fp8_workspace_bytes(B, Hq, Hkv, D, BS, MBS) if B > 0 else 0
+    workspace = _workspace_for(workspace, need, q.device)
+    sc = float(scale) if scale is not None else 0.0
+    rc = load_library().pa_paged_decode_fp8(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), MBS, _ptr(context_lens), B, Hq,
+        Hkv, D, BS, NB, sc, float(k_scale), float(v_scale), _ptr(out), _out_dtype(out),
+        _ptr(workspace), int(workspace.numel()), _stream(q.device))
+    _raise_on("pa_paged_decode_fp8", rc)
 
 
 def paged_prefill(q, k_new, v_new, cu_seqlens_q, block_tables, context_lens, out, *, k_cache,

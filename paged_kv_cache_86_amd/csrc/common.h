@@ -8,6 +8,7 @@ namespace pa {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 8 bf16 = one 128-bit load
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 // Running-max start value: finite, so exp2(m_old - m_new) never sees inf - inf.
@@ -29,19 +30,30 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2, b), c, false);
 }
 
+// Two OCP E4M3 codes (bytes 0,1 or 2,3 of `w`) widened exactly to a bf16 pair
+// (v_cvt_scalef32_pk_bf16_fp8 with scale 1) or to two fp32 (v_cvt_pk_f32_fp8).
+template <bool HIGH>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HIGH));
+}
+template <bool HIGH>
+__device__ __forceinline__ float2_t fp8x2_to_f32x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(w, HIGH);
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
 }
 
-// Sum over aligned groups of N lanes (N = 8 or 16) inside a DPP row; every lane
+// Sum over aligned groups of N lanes (N = 4, 8 or 16) inside a DPP row; every lane
 // of the group ends up holding the group total.
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {
-  static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+  static_assert(N == 4 || N == 8 || N == 16, "group of 4, 8 or 16 lanes");
   v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
   v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
-  v += dpp<0x141>(v);  // row_half_mirror: quads 0<->1 inside each 8
+  if constexpr (N >= 8) v += dpp<0x141>(v);  // row_half_mirror: quads 0<->1 inside each 8
   if constexpr (N == 16) v += dpp<0x140>(v);  // row_mirror: halves 0<->1 inside 16
   return v;
 }

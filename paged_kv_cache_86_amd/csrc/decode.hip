@@ -36,10 +36,18 @@ constexpr int kMaxSplitBlocks = 512;  // split tokens / block size (block size >
 // kWaves * NIT chunks of U * RPW tokens; wave w takes chunks w, w + 4, ...
 // The chunk loop is fully unrolled so that every K/V load of the wave can be
 // issued before the first one is consumed.
-template <int D, int GT, int U, int NIT, bool PRELOAD, bool NT>
+//
+// KV8 selects an FP8 (OCP E4M3) cache: a 16-byte load then carries 16 codes
+// instead of 8 bf16 values.  K codes are widened to bf16 pairs and take the
+// same v_dot2 path as bf16 keys; V codes are widened to fp32.  The per-tensor
+// K scale is folded into the score scale and the V scale into the outputs.
+template <int D, int GT, int U, int NIT, bool PRELOAD, bool NT, bool KV8>
 __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
-  constexpr int LPR = D / 8;     // lanes per K/V row of one head (16 bytes each)
-  constexpr int RPW = 64 / LPR;  // rows per 64-lane load
+  constexpr int EB = KV8 ? 1 : 2;   // bytes per K/V element
+  constexpr int EPL = 16 / EB;      // elements per lane per 16-byte load
+  constexpr int LPR = D / EPL;      // lanes per K/V row of one head
+  constexpr int RPW = 64 / LPR;     // rows per 64-lane load
+  constexpr int QW = EPL / 8;       // 16-byte chunks of q per lane and head
   constexpr int CH = U * RPW;    // tokens per wave chunk
   constexpr int S = kWaves * NIT * CH;  // tokens per split
 
@@ -80,11 +88,13 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
   }
   // Heads past the group's end (last sub-group) re-read its last head; their
   // results are never stored.
-  u32x4 qv[GT];
+  u32x4 qv[GT][QW];
 #pragma unroll
   for (int h = 0; h < GT; ++h) {
     const int hh = h < gh ? h : gh - 1;
-    qv[h] = *(const u32x4*)(a.q + ((int64_t)seq * a.Hq + h0 + hh) * D + c * 8);
+#pragma unroll
+    for (int qw = 0; qw < QW; ++qw)
+      qv[h][qw] = *(const u32x4*)(a.q + ((int64_t)seq * a.Hq + h0 + hh) * D + c * EPL + qw * 8);
   }
   int ctx = a.context_lens[seq];
   const int cap = a.mbs << a.bs_log2;
@@ -106,16 +116,16 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
   __syncthreads();
 
   const int64_t row_stride = (int64_t)a.Hkv * D;
-  const int64_t head_off = (int64_t)kvh * D + c * 8;
+  const int64_t head_off = (int64_t)kvh * D + c * EPL;  // elements
   const int bs_mask = (1 << a.bs_log2) - 1;
 
-  float m[GT], l[GT], acc[GT][8];
+  float m[GT], l[GT], acc[GT][EPL];
 #pragma unroll
   for (int h = 0; h < GT; ++h) {
     m[h] = kNegBig;
     l[h] = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
 
   auto load_chunk = [&](int it, u32x4 (&kc)[U], u32x4 (&vc)[U], bool (&ok)[U]) {
@@ -129,12 +139,14 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
       ok[u] = (j < t1) && (blk >= 0);
       blk = blk < 0 ? 0 : blk;
       const int64_t off = (((int64_t)blk << a.bs_log2) + (jj & bs_mask)) * row_stride + head_off;
+      const u32x4* kp = (const u32x4*)((const char*)a.k_cache + off * EB);
+      const u32x4* vp = (const u32x4*)((const char*)a.v_cache + off * EB);
       if constexpr (NT) {
-        kc[u] = __builtin_nontemporal_load((const u32x4*)(a.k_cache + off));
-        vc[u] = __builtin_nontemporal_load((const u32x4*)(a.v_cache + off));
+        kc[u] = __builtin_nontemporal_load(kp);
+        vc[u] = __builtin_nontemporal_load(vp);
       } else {
-        kc[u] = *(const u32x4*)(a.k_cache + off);
-        vc[u] = *(const u32x4*)(a.v_cache + off);
+        kc[u] = *kp;
+        vc[u] = *vp;
       }
     }
   };
@@ -168,10 +180,23 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
     for (int u = 0; u < U; ++u) {
 #pragma unroll
       for (int h = 0; h < GT; ++h) {
-        float d = dot2_bf16(qv[h].x, kc[u].x, 0.f);
-        d = dot2_bf16(qv[h].y, kc[u].y, d);
-        d = dot2_bf16(qv[h].z, kc[u].z, d);
-        d = dot2_bf16(qv[h].w, kc[u].w, d);
+        float d;
+        if constexpr (KV8) {
+          const uint32_t kw[4] = {kc[u].x, kc[u].y, kc[u].z, kc[u].w};
+          const uint32_t qwv[8] = {qv[h][0].x, qv[h][0].y, qv[h][0].z, qv[h][0].w,
+                                   qv[h][1].x, qv[h][1].y, qv[h][1].z, qv[h][1].w};
+          d = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            d = dot2_bf16(qwv[2 * e], fp8x2_to_bf16x2<false>(kw[e]), d);
+            d = dot2_bf16(qwv[2 * e + 1], fp8x2_to_bf16x2<true>(kw[e]), d);
+          }
+        } else {
+          d = dot2_bf16(qv[h][0].x, kc[u].x, 0.f);
+          d = dot2_bf16(qv[h][0].y, kc[u].y, d);
+          d = dot2_bf16(qv[h][0].z, kc[u].z, d);
+          d = dot2_bf16(qv[h][0].w, kc[u].w, d);
+        }
         d = group_sum<LPR>(d);
         s[u][h] = ok[u] ? d * a.scale_log2e : -INFINITY;
       }
@@ -192,7 +217,7 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
       }
       l[h] = l[h] * alpha + psum;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+      for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -200,16 +225,25 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
       // unused slot from turning 0 * NaN into NaN.
       const uint32_t vw[4] = {ok[u] ? vc[u].x : 0u, ok[u] ? vc[u].y : 0u,
                               ok[u] ? vc[u].z : 0u, ok[u] ? vc[u].w : 0u};
-      float vf[8];
+      float vf[EPL];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        vf[2 * e] = bf16lo(vw[e]);
-        vf[2 * e + 1] = bf16hi(vw[e]);
+        if constexpr (KV8) {
+          const float2_t lo = fp8x2_to_f32x2<false>(vw[e]);
+          const float2_t hi2 = fp8x2_to_f32x2<true>(vw[e]);
+          vf[4 * e] = lo.x;
+          vf[4 * e + 1] = lo.y;
+          vf[4 * e + 2] = hi2.x;
+          vf[4 * e + 3] = hi2.y;
+        } else {
+          vf[2 * e] = bf16lo(vw[e]);
+          vf[2 * e + 1] = bf16hi(vw[e]);
+        }
       }
 #pragma unroll
       for (int h = 0; h < GT; ++h) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(s[u][h], vf[e], acc[h][e]);
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(s[u][h], vf[e], acc[h][e]);
       }
     }
   }
@@ -226,7 +260,7 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
       const float a2 = __builtin_amdgcn_exp2f(mo - mn);
       l[h] = l[h] * a1 + lo * a2;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < EPL; ++e) {
         const float ao = shfl_xor(acc[h][e], off);
         acc[h][e] = acc[h][e] * a1 + ao * a2;
       }
@@ -237,7 +271,7 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int h = 0; h < GT; ++h) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s_acc[w][h][c * 8 + e] = acc[h][e];
+      for (int e = 0; e < EPL; ++e) s_acc[w][h][c * EPL + e] = acc[h][e];
       if (c == 0) {
         s_m[w][h] = m[h];
         s_l[w][h] = l[h];
@@ -260,6 +294,7 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
       L += s_l[ww][h] * f;
       O += s_acc[ww][h][d] * f;
     }
+    if constexpr (KV8) O *= a.v_scale;
     if (nsplit == 1) {
       if (h < gh) {
         const int64_t o = ((int64_t)seq * a.Hq + h0 + h) * D + d;
@@ -352,56 +387,69 @@ __global__ __launch_bounds__(256) void paged_decode_combine_kernel(DecodeArgs a)
 }
 
 // Production tiling (measured on the Qwen3-0.6B-shaped decode, 64 x 16/8 heads,
-// contexts up to 4096): U = 2 rows per lane per chunk, NIT = 8 chunks per wave,
-// every load issued up front, non-temporal (streaming) loads.  That is
-// 256-token splits at D = 128 and 512-token splits at D = 64.
-constexpr int kU = 2;
-constexpr int kNit = 8;
+// contexts up to 4096): every load issued up front, non-temporal (streaming)
+// loads.  bf16: U = 2 rows per lane per chunk, NIT = 8 chunks per wave; FP8:
+// U = 2, NIT = 4 (a 16-byte load carries twice the elements).  Either way a
+// split is 256 tokens at D = 128 and 512 tokens at D = 64.
 constexpr bool kPreload = true;
 constexpr bool kNontemporal = true;
 
-template <int D>
-constexpr int split_tokens() { return kWaves * kNit * kU * (64 / (D / 8)); }
+template <bool KV8> constexpr int tile_u() { return 2; }
+template <bool KV8> constexpr int tile_nit() { return KV8 ? 4 : 8; }
+template <bool KV8> constexpr int max_gt() { return KV8 ? 4 : 8; }
 
-template <int D, int GT>
+template <int D, bool KV8>
+constexpr int split_tokens() {
+  return kWaves * tile_nit<KV8>() * tile_u<KV8>() * (64 / (D / (KV8 ? 16 : 8)));
+}
+
+template <int D, int GT, bool KV8>
 int launch_d(const DecodeArgs& a, int B, hipStream_t stream) {
   const int64_t nwg = (int64_t)B * a.hg * a.nsplit_max;
-  hipLaunchKernelGGL((paged_decode_kernel<D, GT, kU, kNit, kPreload, kNontemporal>), dim3((unsigned)nwg), dim3(256), 0,
-                     stream, a);
+  hipLaunchKernelGGL((paged_decode_kernel<D, GT, tile_u<KV8>(), tile_nit<KV8>(), kPreload,
+                                          kNontemporal, KV8>),
+                     dim3((unsigned)nwg), dim3(256), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return -1;
   if (a.nsplit_max > 1) {
-    hipLaunchKernelGGL((paged_decode_combine_kernel<D, GT, split_tokens<D>()>),
+    hipLaunchKernelGGL((paged_decode_combine_kernel<D, GT, split_tokens<D, KV8>()>),
                        dim3((unsigned)((int64_t)B * a.hg)), dim3(256), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return -1;
   }
   return 0;
 }
 
-template <int D>
+template <int D, bool KV8>
 int launch_gt(const DecodeArgs& a, int B, int gt, hipStream_t stream) {
   switch (gt) {
-    case 1: return launch_d<D, 1>(a, B, stream);
-    case 2: return launch_d<D, 2>(a, B, stream);
-    case 3: return launch_d<D, 3>(a, B, stream);
-    case 4: return launch_d<D, 4>(a, B, stream);
-    case 5: return launch_d<D, 5>(a, B, stream);
-    case 6: return launch_d<D, 6>(a, B, stream);
-    case 7: return launch_d<D, 7>(a, B, stream);
-    case 8: return launch_d<D, 8>(a, B, stream);
-    default: return -2;
+    case 1: return launch_d<D, 1, KV8>(a, B, stream);
+    case 2: return launch_d<D, 2, KV8>(a, B, stream);
+    case 3: return launch_d<D, 3, KV8>(a, B, stream);
+    case 4: return launch_d<D, 4, KV8>(a, B, stream);
+    default:
+      if constexpr (!KV8) {
+        switch (gt) {
+          case 5: return launch_d<D, 5, KV8>(a, B, stream);
+          case 6: return launch_d<D, 6, KV8>(a, B, stream);
+          case 7: return launch_d<D, 7, KV8>(a, B, stream);
+          case 8: return launch_d<D, 8, KV8>(a, B, stream);
+        }
+      }
+      return -2;
   }
 }
 
 }  // namespace
 
-DecodePlan plan_decode(int B, int Hq, int Hkv, int head_dim, int block_size, int mbs) {
+DecodePlan plan_decode(int B, int Hq, int Hkv, int head_dim, int block_size, int mbs, bool kv8) {
   DecodePlan p{};
+  const int gmax = kv8 ? max_gt<true>() : max_gt<false>();
   p.group = Hq / Hkv;
-  p.nsub = (p.group + 7) / 8;
+  p.nsub = (p.group + gmax - 1) / gmax;
   p.gt = (p.group + p.nsub - 1) / p.nsub;
   const int64_t max_ctx = (int64_t)mbs * block_size;
   const int64_t units = (int64_t)B * Hkv * p.nsub;
-  const int S = head_dim == 64 ? split_tokens<64>() : split_tokens<128>();
+  const int S = head_dim == 64 ? (kv8 ? split_tokens<64, true>() : split_tokens<64, false>())
+                               : (kv8 ? split_tokens<128, true>() : split_tokens<128, false>());
   int sl = 0;
   while ((1 << sl) < S) ++sl;
   p.split_log2 = sl;
@@ -415,10 +463,16 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int head_dim, int block_size, int
   return p;
 }
 
-int launch_paged_decode(const DecodeArgs& a, int B, int head_dim, int gt, hipStream_t stream) {
+int launch_paged_decode(const DecodeArgs& a, int B, int head_dim, int gt, bool kv8,
+                        hipStream_t stream) {
   if (B == 0) return 0;
-  if (head_dim == 128) return launch_gt<128>(a, B, gt, stream);
-  if (head_dim == 64) return launch_gt<64>(a, B, gt, stream);
+  if (kv8) {
+    if (head_dim == 128) return launch_gt<128, true>(a, B, gt, stream);
+    if (head_dim == 64) return launch_gt<64, true>(a, B, gt, stream);
+  } else {
+    if (head_dim == 128) return launch_gt<128, false>(a, B, gt, stream);
+    if (head_dim == 64) return launch_gt<64, false>(a, B, gt, stream);
+  }
   return -2;
 }
 

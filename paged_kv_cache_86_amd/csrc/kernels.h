@@ -35,7 +35,8 @@ struct DecodePlan {
   size_t workspace_bytes() const { return ml_bytes + o_bytes; }
 };
 
-DecodePlan plan_decode(int B, int Hq, int Hkv, int head_dim, int block_size, int mbs);
+DecodePlan plan_decode(int B, int Hq, int Hkv, int head_dim, int block_size, int mbs,
+                       bool kv8 = false);
 
 struct DecodeArgs {
   const uint16_t* q;
@@ -47,10 +48,17 @@ struct DecodeArgs {
   float* ws_ml;
   float* ws_o;
   int mbs, Hq, Hkv, group, nsub, hg, bs_log2, split_log2, nsplit_max, num_blocks, out_f32;
-  float scale_log2e;
+  float scale_log2e;  // softmax scale (times the K scale of an FP8 cache) times log2(e)
+  float v_scale;      // V scale of an FP8 cache (1 for bf16)
 };
 
-int launch_paged_decode(const DecodeArgs& args, int B, int head_dim, int gt, hipStream_t stream);
+int launch_paged_decode(const DecodeArgs& args, int B, int head_dim, int gt, bool kv8,
+                        hipStream_t stream);
+
+int launch_kvcache_store_fp8(const void* k, const void* v, const int32_t* slot_mapping, int T,
+                             void* k_cache, void* v_cache, int num_blocks, int block_size,
+                             int num_kv_heads, int head_dim, float k_scale, float v_scale,
+                             hipStream_t stream);
 
 struct PrefillArgs {
   const uint16_t* q;

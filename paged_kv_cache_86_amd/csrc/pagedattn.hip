@@ -63,35 +63,42 @@ int pa_kvcache_store(const void* k, const void* v, const int32_t* slot_mapping, 
              : PA_ERR_HIP;
 }
 
-size_t pa_paged_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
-                                       int head_dim, int block_size, int max_blocks_per_seq) {
+}  // extern "C"
+
+namespace {
+
+size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                              int block_size, int max_blocks_per_seq, bool kv8) {
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
       block_size <= 0 || num_q_heads % num_kv_heads != 0)
     return 0;
   const pa::DecodePlan p = pa::plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                           block_size, max_blocks_per_seq);
+                                           block_size, max_blocks_per_seq, kv8);
   return (p.units > pa::kDecodeMaxUnits || p.nsplit_max > pa::kDecodeMaxSplits)
              ? 0
              : p.workspace_bytes();
 }
 
-int pa_paged_decode(const void* q, const void* k_cache, const void* v_cache,
-                    const int32_t* block_tables, int max_blocks_per_seq,
-                    const int32_t* context_lens, int num_seqs, int num_q_heads,
-                    int num_kv_heads, int head_dim, int block_size, int num_blocks, float scale,
-                    void* out, int out_dtype, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+// Shared body of the bf16 and FP8 decode entry points.  For FP8 the K scale
+// is folded into the score scale and the V scale multiplies the outputs.
+int decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+           int max_blocks_per_seq, const int32_t* context_lens, int num_seqs, int num_q_heads,
+           int num_kv_heads, int head_dim, int block_size, int num_blocks, float scale,
+           bool kv8, float k_scale, float v_scale, void* out, int out_dtype, void* workspace,
+           size_t workspace_bytes, void* stream) {
   if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
   int bs_log2 = 0;
   const int g = check_geometry(num_kv_heads, head_dim, block_size, num_blocks, &bs_log2);
   if (g != PA_OK) return g;
   if (num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
   if (out_dtype != PA_BF16 && out_dtype != PA_F32) return PA_ERR_UNSUPPORTED;
+  if (kv8 && !(k_scale > 0.f && isfinite(k_scale) && v_scale > 0.f && isfinite(v_scale)))
+    return PA_ERR_SHAPE;
   if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX / 2) return PA_ERR_SHAPE;
   if (num_seqs == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PA_ERR_NULL;
   const pa::DecodePlan p = pa::plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                           block_size, max_blocks_per_seq);
+                                           block_size, max_blocks_per_seq, kv8);
   if (!workspace) return PA_ERR_WORKSPACE;
   if (workspace_bytes < p.workspace_bytes()) return PA_ERR_WORKSPACE;
   const int64_t hg = (int64_t)num_kv_heads * p.nsub;
@@ -120,8 +127,69 @@ int pa_paged_decode(const void* q, const void* k_cache, const void* v_cache,
   a.nsplit_max = p.nsplit_max;
   a.num_blocks = num_blocks;
   a.out_f32 = out_dtype == PA_F32;
-  a.scale_log2e = resolve_scale(scale, head_dim) * pa::kLog2eHost;
-  return pa::launch_paged_decode(a, num_seqs, head_dim, p.gt, (hipStream_t)stream) == 0
+  const float sc = resolve_scale(scale, head_dim);
+  a.scale_log2e = (kv8 ? sc * k_scale : sc) * pa::kLog2eHost;
+  a.v_scale = kv8 ? v_scale : 1.f;
+  return pa::launch_paged_decode(a, num_seqs, head_dim, p.gt, kv8, (hipStream_t)stream) == 0
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_paged_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
+                                       int head_dim, int block_size, int max_blocks_per_seq) {
+  return decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                max_blocks_per_seq, false);
+}
+
+size_t pa_paged_decode_fp8_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
+                                           int head_dim, int block_size,
+                                           int max_blocks_per_seq) {
+  return decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                max_blocks_per_seq, true);
+}
+
+int pa_paged_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, int max_blocks_per_seq,
+                    const int32_t* context_lens, int num_seqs, int num_q_heads,
+                    int num_kv_heads, int head_dim, int block_size, int num_blocks, float scale,
+                    void* out, int out_dtype, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  return decode(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, false, 1.f,
+                1.f, out, out_dtype, workspace, workspace_bytes, stream);
+}
+
+int pa_paged_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, int max_blocks_per_seq,
+                        const int32_t* context_lens, int num_seqs, int num_q_heads,
+                        int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                        float scale, float k_scale, float v_scale, void* out, int out_dtype,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  return decode(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, true, k_scale,
+                v_scale, out, out_dtype, workspace, workspace_bytes, stream);
+}
+
+int pa_kvcache_store_fp8(const void* k, const void* v, const int32_t* slot_mapping, int T,
+                         void* k_cache, void* v_cache, int num_blocks, int block_size,
+                         int num_kv_heads, int head_dim, float k_scale, float v_scale,
+                         void* stream) {
+  if (T < 0) return PA_ERR_SHAPE;
+  int bs_log2 = 0;
+  const int g = check_geometry(num_kv_heads, head_dim, block_size, num_blocks, &bs_log2);
+  if (g != PA_OK) return g;
+  if (!(k_scale > 0.f && isfinite(k_scale) && v_scale > 0.f && isfinite(v_scale)))
+    return PA_ERR_SHAPE;
+  if (T == 0) return PA_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PA_ERR_NULL;
+  if ((int64_t)T * num_kv_heads * head_dim / 16 > INT32_MAX) return PA_ERR_SHAPE;
+  return pa::launch_kvcache_store_fp8(k, v, slot_mapping, T, k_cache, v_cache, num_blocks,
+                                      block_size, num_kv_heads, head_dim, k_scale, v_scale,
+                                      (hipStream_t)stream) == 0
              ? PA_OK
              : PA_ERR_HIP;
 }

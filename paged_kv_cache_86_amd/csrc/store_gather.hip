@@ -60,6 +60,65 @@ int launch_kvcache_store(const void* k, const void* v, const int32_t* slot_mappi
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+// FP8 store: each thread turns 16 bf16 values of K (and of V) into 16 OCP
+// E4M3 codes: x / scale in fp32 (correctly rounded division), clamped to
+// +-448 so that large magnitudes saturate (the hardware conversion would give
+// NaN from 480 on), NaN kept as S.1111.111, then v_cvt_pk_fp8_f32 (round to
+// nearest even).  Vector e of token t covers elements 16e .. 16e+15 of its row.
+__device__ __forceinline__ uint32_t fp8_code_pair(float x0, float x1, float s) {
+  float q0 = x0 / s, q1 = x1 / s;
+  const bool n0 = q0 != q0, n1 = q1 != q1;
+  q0 = n0 ? 0.f : fminf(fmaxf(q0, -448.f), 448.f);
+  q1 = n1 ? 0.f : fminf(fmaxf(q1, -448.f), 448.f);
+  uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false) & 0xFFFFu;
+  if (n0) c = (c & 0xFF00u) | 0x7Fu | ((__float_as_uint(x0) >> 24) & 0x80u);
+  if (n1) c = (c & 0x00FFu) | 0x7F00u | ((__float_as_uint(x1) >> 16) & 0x8000u);
+  return c;
+}
+
+__device__ __forceinline__ u32x4 quantize16(const u32x4& a, const u32x4& b, float s) {
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t p0 = fp8_code_pair(bf16lo(w[2 * i]), bf16hi(w[2 * i]), s);
+    const uint32_t p1 = fp8_code_pair(bf16lo(w[2 * i + 1]), bf16hi(w[2 * i + 1]), s);
+    o[i] = p0 | (p1 << 16);
+  }
+  return u32x4{o[0], o[1], o[2], o[3]};
+}
+
+__global__ __launch_bounds__(256) void kvcache_store_fp8_kernel(
+    const u32x4* __restrict__ k, const u32x4* __restrict__ v,
+    const int32_t* __restrict__ slot_mapping, u32x4* __restrict__ k_cache,
+    u32x4* __restrict__ v_cache, int T, int row_vecs8, int64_t num_slots, float k_scale,
+    float v_scale) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)T * row_vecs8) return;
+  const int t = (int)(idx / row_vecs8);
+  const int e = (int)(idx - (int64_t)t * row_vecs8);
+  const int32_t s = slot_mapping[t];
+  if (s < 0 || (int64_t)s >= num_slots) return;
+  const u32x4 k0 = k[2 * idx], k1 = k[2 * idx + 1];
+  const u32x4 v0 = v[2 * idx], v1 = v[2 * idx + 1];
+  k_cache[(int64_t)s * row_vecs8 + e] = quantize16(k0, k1, k_scale);
+  v_cache[(int64_t)s * row_vecs8 + e] = quantize16(v0, v1, v_scale);
+}
+
+int launch_kvcache_store_fp8(const void* k, const void* v, const int32_t* slot_mapping, int T,
+                             void* k_cache, void* v_cache, int num_blocks, int block_size,
+                             int num_kv_heads, int head_dim, float k_scale, float v_scale,
+                             hipStream_t stream) {
+  if (T == 0) return 0;
+  const int row_vecs8 = num_kv_heads * head_dim / 16;
+  const int64_t total = (int64_t)T * row_vecs8;
+  hipLaunchKernelGGL(kvcache_store_fp8_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256),
+                     0, stream, (const u32x4*)k, (const u32x4*)v, slot_mapping, (u32x4*)k_cache,
+                     (u32x4*)v_cache, T, row_vecs8, (int64_t)num_blocks * block_size, k_scale,
+                     v_scale);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 // Un-page: grid (token tiles of 64, sequences).  Thread layout: 64 tokens x
 // `row_vecs` 16-byte vectors, strided by the block size of 256 threads.
 __global__ __launch_bounds__(256) void paged_gather_kernel(

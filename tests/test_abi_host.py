@@ -123,3 +123,48 @@ def test_python_binding_rejects_cpu_tensors():
     cache = torch.zeros(4, 16, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="device"):
         pa.kvcache_store(k, k, torch.zeros(2, dtype=torch.int32), cache, cache)
+
+
+def test_store_fp8_argument_checks(lib):
+    def store8(T=4, D=128, BS=16, ks=1.0, vs=1.0, k=FAKE):
+        return lib.pa_kvcache_store_fp8(k, FAKE, FAKE, T, FAKE, FAKE, 8, BS, 2, D, ks, vs, None)
+    assert store8(T=-1) == PA_ERR_SHAPE
+    assert store8(D=96) == PA_ERR_UNSUPPORTED
+    assert store8(BS=5) == PA_ERR_UNSUPPORTED
+    assert store8(ks=0.0) == PA_ERR_SHAPE
+    assert store8(vs=-2.0) == PA_ERR_SHAPE
+    assert store8(ks=float("inf")) == PA_ERR_SHAPE
+    assert store8(vs=float("nan")) == PA_ERR_SHAPE
+    assert store8(k=None) == PA_ERR_NULL
+    assert store8(T=0, k=None) == PA_OK
+
+
+def test_decode_fp8_argument_checks(lib):
+    def dec8(B=4, Hq=4, Hkv=2, D=128, ks=0.5, vs=0.5, q=FAKE, ws_bytes=None, MBS=8):
+        if ws_bytes is None:
+            ws_bytes = pa.decode_fp8_workspace_bytes(max(B, 1), Hq, Hkv, D, 16, MBS)
+        return lib.pa_paged_decode_fp8(q, FAKE, FAKE, FAKE, MBS, FAKE, B, Hq, Hkv, D, 16, 64, 0.0,
+                                       ks, vs, FAKE, 0, FAKE, ws_bytes, None)
+    assert dec8(Hq=6, Hkv=4) == PA_ERR_SHAPE
+    assert dec8(D=32) == PA_ERR_UNSUPPORTED
+    assert dec8(ks=0.0) == PA_ERR_SHAPE
+    assert dec8(vs=float("inf")) == PA_ERR_SHAPE
+    assert dec8(q=None) == PA_ERR_NULL
+    assert dec8(ws_bytes=8) == PA_ERR_WORKSPACE
+    assert dec8(B=0, q=None) == PA_OK
+    assert dec8(MBS=4097, ws_bytes=1 << 30) == PA_ERR_UNSUPPORTED
+
+
+def test_decode_fp8_workspace_sizes():
+    # Same split length as bf16 (256 tokens at head_dim 128); at most 4 query heads share a
+    # workgroup, so a group of 8 becomes two sub-groups of 4 with the same partial count.
+    assert pa.decode_fp8_workspace_bytes(64, 16, 8, 128, 256, 16) == \
+        pa.decode_workspace_bytes(64, 16, 8, 128, 256, 16)
+    assert pa.decode_fp8_workspace_bytes(64, 64, 8, 128, 16, 64) == \
+        pa.decode_workspace_bytes(64, 64, 8, 128, 16, 64)
+    # a group of 5: bf16 serves it as one workgroup of 5 heads, FP8 as two of 3
+    def ws(parts):  # (max, sum) pairs then 128-float outputs, each region rounded up to 256 B
+        return -(-parts * 8 // 256) * 256 + -(-parts * 512 // 256) * 256
+    assert pa.decode_workspace_bytes(1, 5, 1, 128, 256, 16) == ws(16 * 5)
+    assert pa.decode_fp8_workspace_bytes(1, 5, 1, 128, 256, 16) == ws(16 * 6)
+    assert pa.decode_fp8_workspace_bytes(4, 6, 4, 128, 16, 8) == 0

@@ -1,0 +1,215 @@
+"""FP8 (OCP E4M3) KV cache, HIP path vs the CPU oracle: the quantizing store bit-exact
+(every bfloat16 bit pattern, several scales, workload shapes) and decode on an FP8 pool
+within 1e-2 of attention on the dequantized keys and values."""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_86_amd as pa
+from gpu_util import as_f64, bf16, device, i32, say
+from workloads import config, decode_case
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 1e-2
+
+# A power of two, the typical amax/448 of N(0, 1) data, non-dyadic values, and scales that
+# push almost everything into saturation (tiny) or into the subnormal codes and zero (huge).
+SCALES = [1.0, 0.0107421875, 0.3, 0.017, 2.0 ** -12, 1e-30, 3.7e4, 1e6]
+
+
+def u8(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(dev)
+
+
+def codes(t) -> np.ndarray:
+    return t.cpu().numpy().astype(np.uint8)
+
+
+@pytest.mark.parametrize("ks", SCALES)
+def test_store_fp8_every_bf16_pattern(ks):
+    """All 65536 bf16 bit patterns (NaNs, infinities, subnormals, signed zeros) through the store."""
+    dev = device()
+    D, Hkv = 128, 2
+    T = 65536 // (Hkv * D)
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    k = allbits.reshape(T, Hkv, D)
+    v = allbits[::-1].reshape(T, Hkv, D)
+    vs = 1.0 / ks
+    NB, BS = T // 8 + 3, 8
+    perm = np.random.default_rng(5).permutation(NB * BS)[:T].astype(np.int32)
+    say(f"[fp8-store] every bf16 pattern, k_scale={ks} v_scale={vs}")
+    kc = torch.full((NB, BS, Hkv, D), 0x5A, dtype=torch.uint8, device=dev)
+    vc = torch.full((NB, BS, Hkv, D), 0xA5, dtype=torch.uint8, device=dev)
+    pa.kvcache_store_fp8(bf16(k, dev), bf16(v, dev), i32(perm, dev), kc, vc, ks, vs)
+    want_k, want_v = oracle.kvcache_store_fp8(
+        k, v, perm, np.full((NB, BS, Hkv, D), 0x5A, np.uint8),
+        np.full((NB, BS, Hkv, D), 0xA5, np.uint8), ks, vs)
+    got_k, got_v = codes(kc), codes(vc)
+    bad = np.nonzero(got_k.reshape(-1) != want_k.reshape(-1))[0]
+    if bad.size:
+        i = int(bad[0])
+        flat_slot, within = divmod(i, Hkv * D)
+        t = int(np.nonzero(perm == flat_slot)[0][0])
+        x = int(k.reshape(T, -1)[t, within])
+        say(f"[fp8-store] first K mismatch: bf16 0x{x:04x} -> gpu 0x{got_k.reshape(-1)[i]:02x} "
+            f"oracle 0x{want_k.reshape(-1)[i]:02x} ({bad.size} mismatches)")
+    assert bad.size == 0
+    assert np.array_equal(got_v, want_v)
+
+
+@functools.lru_cache(maxsize=None)
+def workload(cfg_id):
+    say(f"[gen] workload {cfg_id}")
+    return config(cfg_id)
+
+
+def amax_scale(bits) -> float:
+    """Per-tensor scale amax / 448 of the finite values (a test input, not library arithmetic)."""
+    x = oracle.bf16_to_f64(bits)
+    return float(np.float32(np.nanmax(np.abs(x[np.isfinite(x)])) / oracle.E4M3_MAX))
+
+
+class Fp8Pool:
+    """A decode workload with its pools quantized on the GPU by the library's own store."""
+
+    def __init__(self, c, dev, k_scale, v_scale):
+        self.c, self.dev = c, dev
+        self.ks, self.vs = k_scale, v_scale
+        NB, BS, Hkv, D = c.k_cache.shape
+        self.k_cache = torch.empty((NB, BS, Hkv, D), dtype=torch.uint8, device=dev)
+        self.v_cache = torch.empty_like(self.k_cache)
+        every = np.arange(NB * BS, dtype=np.int32)
+        pa.kvcache_store_fp8(bf16(c.k_cache.reshape(NB * BS, Hkv, D), dev),
+                             bf16(c.v_cache.reshape(NB * BS, Hkv, D), dev), i32(every, dev),
+                             self.k_cache, self.v_cache, k_scale, v_scale)
+        self.q = bf16(c.q, dev)
+        self.tables = i32(c.block_tables, dev)
+        self.ctx = i32(c.context_lens, dev)
+        pa.kvcache_store_fp8(bf16(c.k_new, dev), bf16(c.v_new, dev), i32(c.slot_mapping, dev),
+                             self.k_cache, self.v_cache, k_scale, v_scale)
+
+    def oracle_pools(self, blocks):
+        """The oracle's FP8 pools on the given physical blocks (zero codes elsewhere)."""
+        c = self.c
+        kc8 = np.zeros(c.k_cache.shape, np.uint8)
+        vc8 = np.zeros(c.v_cache.shape, np.uint8)
+        kc8[blocks] = oracle.quantize(c.k_cache[blocks], self.ks)
+        vc8[blocks] = oracle.quantize(c.v_cache[blocks], self.vs)
+        return oracle.kvcache_store_fp8(c.k_new, c.v_new, c.slot_mapping, kc8, vc8, self.ks,
+                                        self.vs)
+
+    def decode(self, out_dtype=torch.float32, tables=None, k_cache=None, v_cache=None,
+               workspace=None):
+        c = self.c
+        out = torch.empty((c.batch, c.num_q_heads, c.head_dim), dtype=out_dtype, device=self.dev)
+        pa.paged_decode_fp8(self.q, self.k_cache if k_cache is None else k_cache,
+                            self.v_cache if v_cache is None else v_cache,
+                            self.tables if tables is None else tables, self.ctx, c.scale,
+                            self.ks, self.vs, out, workspace=workspace)
+        return out
+
+
+def check_decode(d: Fp8Pool, rows=None, label=""):
+    c = d.c
+    out32 = as_f64(d.decode(torch.float32))
+    out16 = as_f64(d.decode(torch.bfloat16))
+    rows = list(range(c.batch)) if rows is None else rows
+    # the pools are compared (bit-exact) and read by the oracle only on the sampled rows' blocks
+    blocks = np.unique(c.block_tables[rows][c.block_tables[rows] >= 0])
+    kc8, vc8 = d.oracle_pools(blocks)
+    sel = torch.as_tensor(blocks, dtype=torch.int64, device=d.dev)
+    assert np.array_equal(codes(d.k_cache[sel]), kc8[blocks])
+    assert np.array_equal(codes(d.v_cache[sel]), vc8[blocks])
+    ref = oracle.paged_decode_fp8(c.q[rows], kc8, vc8, c.block_tables[rows], c.context_lens[rows],
+                                  np.float32(c.scale), d.ks, d.vs)
+    e32 = np.abs(out32[rows] - ref).max()
+    e16 = np.abs(out16[rows] - ref).max()
+    say(f"[fp8-decode] {label}: max|err| fp32 {e32:.3e} bf16 {e16:.3e} over {len(rows)} seqs")
+    assert e32 <= ATOL and e16 <= ATOL
+    assert np.all(np.isfinite(out32))
+    return out32, kc8, vc8
+
+
+@pytest.mark.parametrize("cfg_id,limit", [(1, 4), (2, 24), (3, 12)])
+def test_decode_fp8_workload(cfg_id, limit):
+    dev = device()
+    c = workload(cfg_id)
+    ks, vs = amax_scale(c.k_cache), amax_scale(c.v_cache)
+    say(f"[fp8-decode] workload {cfg_id}: B={c.batch} k_scale={ks:.4g} v_scale={vs:.4g}")
+    d = Fp8Pool(c, dev, ks, vs)
+    B = c.batch
+    if B <= limit:
+        rows = list(range(B))
+    else:
+        rng = np.random.default_rng(7)
+        rows = sorted({int(np.argmin(c.context_lens)), int(np.argmax(c.context_lens)),
+                       *map(int, rng.choice(B, limit - 2, replace=False))})
+    check_decode(d, rows, f"workload {cfg_id}")
+
+
+SMALL = [
+    # (D, BS, Hq, Hkv, context lengths)
+    (64, 16, 2, 1, [17, 64, 200, 255, 513]),
+    (64, 1, 4, 4, [1, 2, 3, 70]),
+    (64, 8, 8, 2, [0, 1, 7, 8, 9, 0, 63, 64, 65]),
+    (128, 16, 28, 4, [512, 1, 300, 1024]),          # 7 heads per KV head: sub-groups of 4 and 3
+    (128, 256, 16, 8, [1, 255, 256, 257, 511, 512, 513, 4096]),
+    (128, 32, 5, 1, [129, 33, 2000]),               # 5 heads: sub-groups of 3 and 2
+    (128, 16, 32, 4, [100, 1, 777]),                # 8 heads: two sub-groups of 4
+    (64, 64, 16, 1, [5, 300, 1024]),                # 16 heads: four sub-groups of 4
+    (128, 1024, 2, 2, [3000, 1025]),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"D{c[0]}_bs{c[1]}_h{c[2]}-{c[3]}" for c in SMALL])
+def test_decode_fp8_small_cases(case):
+    dev = device()
+    D, BS, Hq, Hkv, ctx = case
+    c = decode_case(4321 + D + BS + Hq, ctx, Hq, Hkv, D, BS, nb_factor=1.4)
+    say(f"[fp8-decode-small] D={D} BS={BS} Hq={Hq} Hkv={Hkv} ctx={ctx}")
+    d = Fp8Pool(c, dev, 0.0125, 0.02)
+    out32, kc8, vc8 = check_decode(d, label=f"D{D} bs{BS}")
+    G = Hq // Hkv
+    for i, n in enumerate(ctx):
+        if n == 0:
+            assert np.all(out32[i] == 0)
+        if n == 1:  # one key: the output is that token's V, code * v_scale rounded to fp32
+            blk, off = divmod(int(c.slot_mapping[i]), BS)
+            vrow = np.float32(oracle.e4m3_decode(vc8[blk, off]) * np.float32(d.vs))
+            for h in range(Hq):
+                assert np.array_equal(out32[i, h], vrow[h // G].astype(np.float64))
+
+
+def test_decode_fp8_block_permutation_bit_identical():
+    dev = device()
+    c = decode_case(91, [300, 1, 513, 40, 1024], 8, 2, 128, 16, nb_factor=1.5)
+    d = Fp8Pool(c, dev, 0.0125, 0.02)
+    a = d.decode(torch.float32)
+    perm = np.random.default_rng(92).permutation(c.num_blocks)
+    kc, vc = codes(d.k_cache), codes(d.v_cache)
+    kp, vp = np.empty_like(kc), np.empty_like(vc)
+    kp[perm] = kc
+    vp[perm] = vc
+    bt = np.where(c.block_tables >= 0, perm[np.maximum(c.block_tables, 0)], -1)
+    b = d.decode(torch.float32, tables=i32(bt, dev), k_cache=u8(kp, dev), v_cache=u8(vp, dev))
+    assert torch.equal(a, b)
+    assert torch.equal(a, d.decode(torch.float32))  # deterministic
+
+
+def test_decode_fp8_scales_fold_exactly():
+    """Scaling k_scale by 2 and the softmax scale by 1/2 leaves the scores, hence outputs, unchanged;
+    scaling v_scale by 2 doubles the outputs exactly (powers of two are exact in fp32)."""
+    dev = device()
+    c = decode_case(93, [700, 64, 1], 8, 4, 64, 16, nb_factor=1.3)
+    d = Fp8Pool(c, dev, 0.0125, 0.02)
+    base = d.decode(torch.float32)
+    out = torch.empty_like(base)
+    pa.paged_decode_fp8(d.q, d.k_cache, d.v_cache, d.tables, d.ctx, c.scale / 2, d.ks * 2, d.vs,
+                        out)
+    assert torch.equal(out, base)
+    pa.paged_decode_fp8(d.q, d.k_cache, d.v_cache, d.tables, d.ctx, c.scale, d.ks, d.vs * 2, out)
+    assert torch.equal(out, base * 2)

@@ -1,8 +1,9 @@
 """Benchmark of the paged-KV attention hot path on one MI355X.
 
 A step is one pass of the hot path over one batch: kvcache_store of the new
-token of each sequence, then paged_decode, on the Qwen3-0.6B-shaped decode
-workload (64 sequences, 16 query / 8 KV heads, head_dim 128, block 256,
+token of each sequence, then paged_decode (one fused paged_decode_append
+call; the separate store + decode calls are timed alongside), on the
+Qwen3-0.6B-shaped decode workload (64 sequences, 16 query / 8 KV heads, head_dim 128, block 256,
 context lengths uniform on [128, 4096], 2048-block pool).  Inputs are seeded
 synthetic bf16 N(0, 1) values resident in HBM before timing starts.
 
@@ -10,9 +11,10 @@ Before every timed step a 512 MiB fill evicts the 256 MB Infinity Cache and
 the L2s (outside the timed events), so each step reads its K/V from HBM.
 Per-step times come from HIP events on the stream the kernels run on.
 
-Prints one JSON line.  Extra legs: the prefix-hit prefill workload (16 x 512
-new tokens over prefixes of up to 3584 tokens) timed the same way, and the
-CPU oracle timed on a bounded sample of the decode workload.
+Prints one JSON line.  Extra legs: the same decode step on an FP8 (E4M3) copy
+of the cache, the prefix-hit prefill workload (16 x 512 new tokens over
+prefixes of up to 3584 tokens) timed the same way, and the CPU oracle timed
+on a bounded sample of the decode workload.
 """
 from __future__ import annotations
 
@@ -40,6 +42,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--copy-probe", action="store_true",
@@ -214,11 +217,20 @@ def main():
     def decode():
         pa.paged_decode(q, kc, vc, tables, ctx, c.scale, out, workspace=ws)
 
-    ms_step, ms_dec, dec_ms, wall = timed_loop(torch, store, decode, args.steps, args.warmup,
-                                               flush)
+    def append():
+        pa.paged_decode_append(q, k_new, v_new, slots, kc, vc, tables, ctx, c.scale, out,
+                               workspace=ws)
+
+    def nothing():
+        pass
+
+    # the step: fused store + decode
+    ms_step, _, step_ms, wall = timed_loop(torch, nothing, append, args.steps, args.warmup, flush)
+    # the same work as two calls, and decode alone
+    ms_pair, ms_dec, dec_ms, _ = timed_loop(torch, store, decode, args.steps, args.warmup, flush)
     kv_bytes = c.kv_bytes()
-    alg = decode_algorithmic_bytes(c)
-    achieved = alg / (ms_dec * 1e-3) / 1e9
+    alg = decode_algorithmic_bytes(c) + store_bytes(c)
+    achieved = alg / (ms_step * 1e-3) / 1e9
     traffic = counter_traffic(args.traffic)
 
     result = {
@@ -242,18 +254,60 @@ def main():
                    "seed": c.seed},
         "pct_hbm_peak": round(100 * kv_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(c.batch / (ms_step * 1e-3), 1),
-        "decode_ms": round(ms_dec, 5),
-        "decode_ms_per_call_events": {"min": round(float(np.min(dec_ms)), 5),
-                                      "median": round(float(np.median(dec_ms)), 5),
-                                      "p90": round(float(np.percentile(dec_ms, 90)), 5)},
-        "store_ms": round(ms_step - ms_dec, 5),
+        "ms_per_step_events": {"min": round(float(np.min(step_ms)), 5),
+                               "median": round(float(np.median(step_ms)), 5),
+                               "p90": round(float(np.percentile(step_ms, 90)), 5)},
+        "unfused": {"ms_per_step_store_then_decode": round(ms_pair, 5),
+                    "decode_ms": round(ms_dec, 5),
+                    "store_ms": round(ms_pair - ms_dec, 5),
+                    "decode_kv_gb_s": round(kv_bytes / (ms_dec * 1e-3) / 1e9, 2),
+                    "decode_ms_per_call_events_median": round(float(np.median(dec_ms)), 5)},
         "wall_s_timed_region_incl_flush": round(wall, 4),
-        "roofline": {"kernel": "paged_decode_kernel + paged_decode_combine_kernel (one decode call)",
+        "roofline": {"kernel": "paged_decode_kernel (append) + paged_decode_combine_kernel "
+                               "(one paged_decode_append call)",
                      "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": alg},
     }
+
+    # ---------------------------------------------------------------- FP8 cache (extra leg)
+    if not args.no_fp8:
+        # The bf16 pools quantized by the library's own store; one fixed per-tensor scale of
+        # 1/64 for N(0, 1) data (codes reach +-448, i.e. values up to +-7).
+        fscale = 1.0 / 64
+        NB, BS, Hkv, D = c.k_cache.shape
+        k8 = torch.empty((NB, BS, Hkv, D), dtype=torch.uint8, device=dev)
+        v8 = torch.empty_like(k8)
+        every = torch.arange(NB * BS, dtype=torch.int32, device=dev)
+        pa.kvcache_store_fp8(kc.view(NB * BS, Hkv, D), vc.view(NB * BS, Hkv, D), every, k8, v8,
+                             fscale, fscale)
+        del every
+        ws8 = torch.empty(pa.decode_fp8_workspace_bytes(c.batch, c.num_q_heads, c.num_kv_heads,
+                                                        c.head_dim, c.block_size,
+                                                        c.max_blocks_per_seq),
+                          dtype=torch.uint8, device=dev)
+
+        def append8():
+            pa.paged_decode_append_fp8(q, k_new, v_new, slots, k8, v8, tables, ctx, c.scale,
+                                       fscale, fscale, out, workspace=ws8)
+
+        fstep, _, fev, _ = timed_loop(torch, nothing, append8, args.steps, args.warmup, flush)
+        kv8 = kv_bytes // 2
+        # K/V codes instead of bf16; the new rows are read as bf16 and written as codes
+        alg8 = alg - kv_bytes + kv8 - store_bytes(c) // 4
+        result["fp8_decode"] = {
+            "workload": "same decode step (fused store + decode), K/V cache in OCP FP8 E4M3 "
+                        "(per-tensor scale 1/64)",
+            "ms_per_step": round(fstep, 5),
+            "ms_per_step_events_median": round(float(np.median(fev)), 5),
+            "kv_gb_s": round(kv8 / (fstep * 1e-3) / 1e9, 2),
+            "achieved_gb_s": round(alg8 / (fstep * 1e-3) / 1e9, 2),
+            "frac_hbm_peak": round(alg8 / (fstep * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes_per_launch": alg8,
+            "tokens_per_s": round(c.batch / (fstep * 1e-3), 1),
+            "speedup_vs_bf16_step": round(ms_step / fstep, 3)}
+        del k8, v8
 
     # ---------------------------------------------------------------- prefill (extra leg)
     if not args.no_prefill:

@@ -117,6 +117,28 @@ int pa_paged_decode(const void* q, const void* k_cache, const void* v_cache,
                     void* stream);
 
 /*
+ * Fused store + decode: the effect of pa_kvcache_store(k_new, v_new,
+ * slot_mapping, T = num_seqs) followed by pa_paged_decode, in one call that
+ * launches the decode kernels only (MinivLLM guide §4.5 prepare_decode: each
+ * decode step appends one token per sequence at slot_mapping[i] and then
+ * attends over its context_lens[i] tokens).
+ *   k_new, v_new  [num_seqs, num_kv_heads, head_dim] bf16: the new token of each sequence
+ *   slot_mapping  [num_seqs] int32; < 0 or >= num_blocks*block_size stores nothing
+ *   k_cache, v_cache  updated in place at those slots; everything else as pa_paged_decode
+ * Position context_lens[i]-1 (the new token) is taken from k_new/v_new rather
+ * than read back from the cache, so the result equals store-then-decode when
+ * slot_mapping[i] is that position's slot under block_tables[i], which is
+ * what a decode step passes.  Workspace: pa_paged_decode_workspace_bytes.
+ */
+int pa_paged_decode_append(const void* q, const void* k_new, const void* v_new,
+                           const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                           const int32_t* block_tables, int max_blocks_per_seq,
+                           const int32_t* context_lens, int num_seqs, int num_q_heads,
+                           int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                           float scale, void* out, int out_dtype, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
  * FP8 KV cache (VLLM 0.7.3 source article §5.3, KV cache precision: the cache
  * is stored in FP8 while attention outputs stay in high precision).  The page
  * fixes neither format nor scaling; this library uses OCP FP8 E4M3 codes
@@ -157,6 +179,21 @@ int pa_paged_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
                         int num_kv_heads, int head_dim, int block_size, int num_blocks,
                         float scale, float k_scale, float v_scale, void* out, int out_dtype,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Fused store + decode on FP8 pools: pa_kvcache_store_fp8 followed by
+ * pa_paged_decode_fp8 (same scales for both), in one call.  The new token is
+ * quantized exactly as the store does and attended from those codes.
+ * Workspace: pa_paged_decode_fp8_workspace_bytes.
+ */
+int pa_paged_decode_append_fp8(const void* q, const void* k_new, const void* v_new,
+                               const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                               const int32_t* block_tables, int max_blocks_per_seq,
+                               const int32_t* context_lens, int num_seqs, int num_q_heads,
+                               int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                               float scale, float k_scale, float v_scale, void* out,
+                               int out_dtype, void* workspace, size_t workspace_bytes,
+                               void* stream);
 
 /*
  * Prefix-hit prefill ("Nano-vLLM源码学习(2)" §2: the prefix-hit prefill path

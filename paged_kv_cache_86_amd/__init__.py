@@ -33,6 +33,8 @@ EXPORTED_SYMBOLS = (
     "pa_kvcache_store_fp8",
     "pa_paged_decode_fp8_workspace_bytes",
     "pa_paged_decode_fp8",
+    "pa_paged_decode_append",
+    "pa_paged_decode_append_fp8",
 )
 
 _lib = None
@@ -74,6 +76,12 @@ def load_library() -> ctypes.CDLL:
     lib.pa_paged_decode_fp8.argtypes = [P, P, P, P, I, P, I, I, I, I, I, I, F, F, F, P, I, P, Z,
                                         P]
     lib.pa_paged_decode_fp8.restype = I
+    lib.pa_paged_decode_append.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, F, P, I,
+                                           P, Z, P]
+    lib.pa_paged_decode_append.restype = I
+    lib.pa_paged_decode_append_fp8.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, F,
+                                               F, F, P, I, P, Z, P]
+    lib.pa_paged_decode_append_fp8.restype = I
     _lib = lib
     return lib
 
@@ -209,6 +217,33 @@ def paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale: Optiona
     _raise_on("pa_paged_decode", rc)
 
 
+def _new_tokens(k_new, v_new, slot_mapping, B, Hkv, D):
+    torch = _torch()
+    _check(k_new, torch.bfloat16, "k_new", 3)
+    _check(v_new, torch.bfloat16, "v_new", 3)
+    _check(slot_mapping, torch.int32, "slot_mapping", 1)
+    if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
+        raise ValueError(f"k_new and v_new must be [{B}, {Hkv}, {D}]")
+    if slot_mapping.shape[0] != B:
+        raise ValueError("slot_mapping must have one entry per sequence")
+
+
+def paged_decode_append(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
+                        context_lens, scale: Optional[float], out, workspace=None) -> None:
+    """kvcache_store of each sequence's new token followed by paged_decode, in one call."""
+    NB, BS, Hkv, D = _cache_geometry(k_cache, v_cache)
+    B, Hq, MBS = _decode_shapes(q, block_tables, context_lens, out, D)
+    _new_tokens(k_new, v_new, slot_mapping, B, Hkv, D)
+    need = decode_workspace_bytes(B, Hq, Hkv, D, BS, MBS) if B > 0 else 0
+    workspace = _workspace_for(workspace, need, q.device)
+    sc = float(scale) if scale is not None else 0.0
+    rc = load_library().pa_paged_decode_append(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache),
+        _ptr(block_tables), MBS, _ptr(context_lens), B, Hq, Hkv, D, BS, NB, sc, _ptr(out),
+        _out_dtype(out), _ptr(workspace), int(workspace.numel()), _stream(q.device))
+    _raise_on("pa_paged_decode_append", rc)
+
+
 def kvcache_store_fp8(k, v, slot_mapping, k_cache, v_cache, k_scale: float,
                       v_scale: float) -> None:
     """Quantize row t of k/v to E4M3 codes (x / scale) into uint8 cache slot ``slot_mapping[t]``."""
@@ -304,3 +339,22 @@ def default_scale(head_dim: int) -> float:
     """1/sqrt(head_dim) rounded to float32, the value the kernels use for scale <= 0."""
     import struct
     return struct.unpack("f", struct.pack("f", 1.0 / math.sqrt(head_dim)))[0]
+
+
+def paged_decode_append_fp8(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
+                            context_lens, scale: Optional[float], k_scale: float, v_scale: float,
+                            out, workspace=None) -> None:
+    """kvcache_store_fp8 of each sequence's new token followed by paged_decode_fp8, in one call."""
+    torch = _torch()
+    NB, BS, Hkv, D = _cache_geometry(k_cache, v_cache, torch.uint8)
+    B, Hq, MBS = _decode_shapes(q, block_tables, context_lens, out, D)
+    _new_tokens(k_new, v_new, slot_mapping, B, Hkv, D)
+    need = decode_fp8_workspace_bytes(B, Hq, Hkv, D, BS, MBS) if B > 0 else 0
+    workspace = _workspace_for(workspace, need, q.device)
+    sc = float(scale) if scale is not None else 0.0
+    rc = load_library().pa_paged_decode_append_fp8(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache),
+        _ptr(block_tables), MBS, _ptr(context_lens), B, Hq, Hkv, D, BS, NB, sc, float(k_scale),
+        float(v_scale), _ptr(out), _out_dtype(out), _ptr(workspace), int(workspace.numel()),
+        _stream(q.device))
+    _raise_on("pa_paged_decode_append_fp8", rc)

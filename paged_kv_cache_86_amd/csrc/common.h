@@ -7,6 +7,7 @@
 namespace pa {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 8 bf16 = one 128-bit load
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 
@@ -24,6 +25,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+// A rounded fp32 product that is never contracted into a later add or
+// subtract (hipcc contracts a * b - c into one fma by default, and
+// __fmul_rn is a plain multiply that contracts the same way).
+__device__ __forceinline__ float mul_rn(float a, float b) {
+#pragma clang fp contract(off)
+  return a * b;
+}
+
 // Two bf16 products summed into an fp32 accumulator (v_dot2_f32_bf16).
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
@@ -39,6 +48,34 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
 template <bool HIGH>
 __device__ __forceinline__ float2_t fp8x2_to_f32x2(uint32_t w) {
   return __builtin_amdgcn_cvt_pk_f32_fp8(w, HIGH);
+}
+
+// bf16 -> OCP E4M3 code of x / s: the division in fp32 (correctly rounded),
+// clamped to +-448 so that large magnitudes saturate (the hardware conversion
+// would give NaN from 480 on), NaN kept as S.1111.111 with the input's sign,
+// then v_cvt_pk_fp8_f32 (round to nearest even).  Two codes in bits 0..15.
+__device__ __forceinline__ uint32_t fp8_code_pair(float x0, float x1, float s) {
+  float q0 = x0 / s, q1 = x1 / s;
+  const bool n0 = q0 != q0, n1 = q1 != q1;
+  q0 = n0 ? 0.f : fminf(fmaxf(q0, -448.f), 448.f);
+  q1 = n1 ? 0.f : fminf(fmaxf(q1, -448.f), 448.f);
+  uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false) & 0xFFFFu;
+  if (n0) c = (c & 0xFF00u) | 0x7Fu | ((__float_as_uint(x0) >> 24) & 0x80u);
+  if (n1) c = (c & 0x00FFu) | 0x7F00u | ((__float_as_uint(x1) >> 16) & 0x8000u);
+  return c;
+}
+
+// Eight bf16 values (one 16-byte vector) -> eight E4M3 codes, in element order.
+__device__ __forceinline__ u32x2 quantize8(const u32x4& a, float s) {
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+  uint32_t o[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t p0 = fp8_code_pair(bf16lo(w[2 * i]), bf16hi(w[2 * i]), s);
+    const uint32_t p1 = fp8_code_pair(bf16lo(w[2 * i + 1]), bf16hi(w[2 * i + 1]), s);
+    o[i] = p0 | (p1 << 16);
+  }
+  return u32x2{o[0], o[1]};
 }
 
 template <int CTRL>

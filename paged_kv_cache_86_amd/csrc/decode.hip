@@ -41,7 +41,13 @@ constexpr int kMaxSplitBlocks = 512;  // split tokens / block size (block size >
 // instead of 8 bf16 values.  K codes are widened to bf16 pairs and take the
 // same v_dot2 path as bf16 keys; V codes are widened to fp32.  The per-tensor
 // K scale is folded into the score scale and the V scale into the outputs.
-template <int D, int GT, int U, int NIT, bool PRELOAD, bool NT, bool KV8>
+//
+// APPEND fuses the store of each sequence's new token: position ctx-1 is not
+// read from the cache but from k_new / v_new (quantized first for KV8, exactly
+// as the store kernel does), staged in LDS and folded into the softmax state
+// of the split that holds it; the workgroup of that split with sub-group 0
+// also writes the row into its cache slot.
+template <int D, int GT, int U, int NIT, bool PRELOAD, bool NT, bool KV8, bool APPEND>
 __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
   constexpr int EB = KV8 ? 1 : 2;   // bytes per K/V element
   constexpr int EPL = 16 / EB;      // elements per lane per 16-byte load
@@ -55,6 +61,8 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
   __shared__ float s_m[kWaves][GT];
   __shared__ float s_l[kWaves][GT];
   __shared__ float s_acc[kWaves][GT][D];
+  constexpr int NLB = D / 8;  // 16-byte bf16 vectors per new K (or V) row of one head
+  __shared__ u32x4 s_new[APPEND ? 2 : 1][APPEND ? NLB : 1];  // new K, V row (bf16 or codes)
 
   const int bid = blockIdx.x;
   const int hg = bid % a.hg;
@@ -96,9 +104,41 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
     for (int qw = 0; qw < QW; ++qw)
       qv[h][qw] = *(const u32x4*)(a.q + ((int64_t)seq * a.Hq + h0 + hh) * D + c * EPL + qw * 8);
   }
+  // APPEND: threads 0 .. 2*NLB-1 fetch one 16-byte vector of the new K (V) row
+  // of this KV head, and the sequence's slot.
+  const bool new_lane = APPEND && tid < 2 * NLB;
+  const bool new_is_v = tid >= NLB;
+  const int new_c = new_is_v ? tid - NLB : tid;
+  u32x4 xnew{};
+  int slot = -1;
+  if constexpr (APPEND) {
+    if (new_lane) {
+      const uint16_t* src = new_is_v ? a.v_new : a.k_new;
+      xnew = *(const u32x4*)(src + ((int64_t)seq * a.Hkv + kvh) * D + new_c * 8);
+      slot = a.slot_mapping[seq];
+    }
+  }
   int ctx = a.context_lens[seq];
   const int cap = a.mbs << a.bs_log2;
   ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+  const int nsplit = ctx == 0 ? 1 : (ctx + S - 1) / S;
+
+  // APPEND: the workgroup of the last split stages the new row (as codes for
+  // KV8) in LDS; the one of sub-group 0 also stores it into the cache.
+  if constexpr (APPEND) {
+    if (new_lane && split == nsplit - 1) {
+      const int64_t dst = ((int64_t)slot * a.Hkv + kvh) * D + new_c * 8;  // element index
+      const bool store = sub == 0 && slot >= 0 && (int64_t)slot < a.num_slots;
+      if constexpr (KV8) {
+        const u32x2 cw = quantize8(xnew, new_is_v ? a.qscale_v : a.qscale_k);
+        ((u32x2*)&s_new[new_is_v][0])[new_c] = cw;
+        if (store) *(u32x2*)((char*)(new_is_v ? a.v_cache_w : a.k_cache_w) + dst) = cw;
+      } else {
+        s_new[new_is_v][new_c] = xnew;
+        if (store) *(u32x4*)((uint16_t*)(new_is_v ? a.v_cache_w : a.k_cache_w) + dst) = xnew;
+      }
+    }
+  }
 
   if (ctx == 0) {  // padded row: output zeros
     if (split == 0) {
@@ -110,9 +150,13 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
     }
     return;
   }
-  const int nsplit = (ctx + S - 1) / S;
   if (split >= nsplit) return;
-  const int t1 = min(ctx, t0 + S);
+  // Cached tokens of this split are t0 .. t1-1 (with APPEND the last position
+  // comes from k_new / v_new instead; t1 <= t0 when the split holds only it).
+  // Loads past t1 re-read row `jfill`, which is in bounds and masked out.
+  const int tc = APPEND ? ctx - 1 : ctx;
+  const int t1 = min(tc, t0 + S);
+  const int jfill = t1 > t0 ? t1 - 1 : t0;
   __syncthreads();
 
   const int64_t row_stride = (int64_t)a.Hkv * D;
@@ -128,13 +172,52 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
 
+  // Partial q.k of query head h over this lane's EPL elements of one K row.
+  auto kdot = [&](int h, const u32x4& k) -> float {
+    float d = 0.f;
+    if constexpr (KV8) {
+      const uint32_t kw[4] = {k.x, k.y, k.z, k.w};
+      const uint32_t qwv[8] = {qv[h][0].x, qv[h][0].y, qv[h][0].z, qv[h][0].w,
+                               qv[h][QW - 1].x, qv[h][QW - 1].y, qv[h][QW - 1].z, qv[h][QW - 1].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        d = dot2_bf16(qwv[2 * e], fp8x2_to_bf16x2<false>(kw[e]), d);
+        d = dot2_bf16(qwv[2 * e + 1], fp8x2_to_bf16x2<true>(kw[e]), d);
+      }
+    } else {
+      d = dot2_bf16(qv[h][0].x, k.x, d);
+      d = dot2_bf16(qv[h][0].y, k.y, d);
+      d = dot2_bf16(qv[h][0].z, k.z, d);
+      d = dot2_bf16(qv[h][0].w, k.w, d);
+    }
+    return d;
+  };
+  // This lane's EPL elements of one V row as fp32.
+  auto vconv = [&](const u32x4& v, float (&vf)[EPL]) {
+    const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (KV8) {
+        const float2_t lo = fp8x2_to_f32x2<false>(vw[e]);
+        const float2_t hi = fp8x2_to_f32x2<true>(vw[e]);
+        vf[4 * e] = lo.x;
+        vf[4 * e + 1] = lo.y;
+        vf[4 * e + 2] = hi.x;
+        vf[4 * e + 3] = hi.y;
+      } else {
+        vf[2 * e] = bf16lo(vw[e]);
+        vf[2 * e + 1] = bf16hi(vw[e]);
+      }
+    }
+  };
+
   auto load_chunk = [&](int it, u32x4 (&kc)[U], u32x4 (&vc)[U], bool (&ok)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       // Rows past the split end re-read the split's last row (in bounds, finite) and
       // are masked out of the softmax below.
       const int j = t0 + (it * kWaves + w) * CH + u * RPW + r;
-      const int jj = j < t1 ? j : t1 - 1;
+      const int jj = j < t1 ? j : jfill;
       int blk = s_blk[(jj >> a.bs_log2) - b0];
       ok[u] = (j < t1) && (blk >= 0);
       blk = blk < 0 ? 0 : blk;
@@ -180,25 +263,10 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
     for (int u = 0; u < U; ++u) {
 #pragma unroll
       for (int h = 0; h < GT; ++h) {
-        float d;
-        if constexpr (KV8) {
-          const uint32_t kw[4] = {kc[u].x, kc[u].y, kc[u].z, kc[u].w};
-          const uint32_t qwv[8] = {qv[h][0].x, qv[h][0].y, qv[h][0].z, qv[h][0].w,
-                                   qv[h][1].x, qv[h][1].y, qv[h][1].z, qv[h][1].w};
-          d = 0.f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            d = dot2_bf16(qwv[2 * e], fp8x2_to_bf16x2<false>(kw[e]), d);
-            d = dot2_bf16(qwv[2 * e + 1], fp8x2_to_bf16x2<true>(kw[e]), d);
-          }
-        } else {
-          d = dot2_bf16(qv[h][0].x, kc[u].x, 0.f);
-          d = dot2_bf16(qv[h][0].y, kc[u].y, d);
-          d = dot2_bf16(qv[h][0].z, kc[u].z, d);
-          d = dot2_bf16(qv[h][0].w, kc[u].w, d);
-        }
-        d = group_sum<LPR>(d);
-        s[u][h] = ok[u] ? d * a.scale_log2e : -INFINITY;
+        const float d = group_sum<LPR>(kdot(h, kc[u]));
+        // mul_rn: the score is rounded once and the same value is compared
+        // with and subtracted from the running max (the maximum gives p = 1).
+        s[u][h] = ok[u] ? mul_rn(d, a.scale_log2e) : -INFINITY;
       }
     }
 #pragma unroll
@@ -223,27 +291,44 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
     for (int u = 0; u < U; ++u) {
       // Masked rows contribute p = 0; zeroing V as well keeps a NaN in an
       // unused slot from turning 0 * NaN into NaN.
-      const uint32_t vw[4] = {ok[u] ? vc[u].x : 0u, ok[u] ? vc[u].y : 0u,
-                              ok[u] ? vc[u].z : 0u, ok[u] ? vc[u].w : 0u};
+      // (Selected per component: a select of the whole vector makes the
+      // compiler keep extra copies of the preloaded rows live.)
+      u32x4 vm;
+      vm.x = ok[u] ? vc[u].x : 0u;
+      vm.y = ok[u] ? vc[u].y : 0u;
+      vm.z = ok[u] ? vc[u].z : 0u;
+      vm.w = ok[u] ? vc[u].w : 0u;
       float vf[EPL];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (KV8) {
-          const float2_t lo = fp8x2_to_f32x2<false>(vw[e]);
-          const float2_t hi2 = fp8x2_to_f32x2<true>(vw[e]);
-          vf[4 * e] = lo.x;
-          vf[4 * e + 1] = lo.y;
-          vf[4 * e + 2] = hi2.x;
-          vf[4 * e + 3] = hi2.y;
-        } else {
-          vf[2 * e] = bf16lo(vw[e]);
-          vf[2 * e + 1] = bf16hi(vw[e]);
-        }
-      }
+      vconv(vm, vf);
 #pragma unroll
       for (int h = 0; h < GT; ++h) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(s[u][h], vf[e], acc[h][e]);
+      }
+    }
+  }
+
+  // APPEND: row slot 0 of wave 0 takes the new token (last split only).
+  if constexpr (APPEND) {
+    if (split == nsplit - 1 && w == 0) {
+      const u32x4 kx = s_new[0][c];
+      const u32x4 vx = s_new[1][c];
+      float sn[GT];
+#pragma unroll
+      for (int h = 0; h < GT; ++h) sn[h] = mul_rn(group_sum<LPR>(kdot(h, kx)), a.scale_log2e);
+      if (r == 0) {
+        float vf[EPL];
+        vconv(vx, vf);
+#pragma unroll
+        for (int h = 0; h < GT; ++h) {
+          const float mnew = fmaxf(m[h], sn[h]);
+          const float alpha = __builtin_amdgcn_exp2f(m[h] - mnew);
+          const float p = __builtin_amdgcn_exp2f(sn[h] - mnew);
+          m[h] = mnew;
+          l[h] = l[h] * alpha + p;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e] * alpha);
+        }
       }
     }
   }
@@ -403,11 +488,11 @@ constexpr int split_tokens() {
   return kWaves * tile_nit<KV8>() * tile_u<KV8>() * (64 / (D / (KV8 ? 16 : 8)));
 }
 
-template <int D, int GT, bool KV8>
+template <int D, int GT, bool KV8, bool APPEND>
 int launch_d(const DecodeArgs& a, int B, hipStream_t stream) {
   const int64_t nwg = (int64_t)B * a.hg * a.nsplit_max;
   hipLaunchKernelGGL((paged_decode_kernel<D, GT, tile_u<KV8>(), tile_nit<KV8>(), kPreload,
-                                          kNontemporal, KV8>),
+                                          kNontemporal, KV8, APPEND>),
                      dim3((unsigned)nwg), dim3(256), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return -1;
   if (a.nsplit_max > 1) {
@@ -418,24 +503,31 @@ int launch_d(const DecodeArgs& a, int B, hipStream_t stream) {
   return 0;
 }
 
-template <int D, bool KV8>
+template <int D, bool KV8, bool APPEND>
 int launch_gt(const DecodeArgs& a, int B, int gt, hipStream_t stream) {
   switch (gt) {
-    case 1: return launch_d<D, 1, KV8>(a, B, stream);
-    case 2: return launch_d<D, 2, KV8>(a, B, stream);
-    case 3: return launch_d<D, 3, KV8>(a, B, stream);
-    case 4: return launch_d<D, 4, KV8>(a, B, stream);
+    case 1: return launch_d<D, 1, KV8, APPEND>(a, B, stream);
+    case 2: return launch_d<D, 2, KV8, APPEND>(a, B, stream);
+    case 3: return launch_d<D, 3, KV8, APPEND>(a, B, stream);
+    case 4: return launch_d<D, 4, KV8, APPEND>(a, B, stream);
     default:
       if constexpr (!KV8) {
         switch (gt) {
-          case 5: return launch_d<D, 5, KV8>(a, B, stream);
-          case 6: return launch_d<D, 6, KV8>(a, B, stream);
-          case 7: return launch_d<D, 7, KV8>(a, B, stream);
-          case 8: return launch_d<D, 8, KV8>(a, B, stream);
+          case 5: return launch_d<D, 5, KV8, APPEND>(a, B, stream);
+          case 6: return launch_d<D, 6, KV8, APPEND>(a, B, stream);
+          case 7: return launch_d<D, 7, KV8, APPEND>(a, B, stream);
+          case 8: return launch_d<D, 8, KV8, APPEND>(a, B, stream);
         }
       }
       return -2;
   }
+}
+
+template <bool KV8, bool APPEND>
+int launch_head_dim(const DecodeArgs& a, int B, int head_dim, int gt, hipStream_t stream) {
+  if (head_dim == 128) return launch_gt<128, KV8, APPEND>(a, B, gt, stream);
+  if (head_dim == 64) return launch_gt<64, KV8, APPEND>(a, B, gt, stream);
+  return -2;
 }
 
 }  // namespace
@@ -463,17 +555,15 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int head_dim, int block_size, int
   return p;
 }
 
-int launch_paged_decode(const DecodeArgs& a, int B, int head_dim, int gt, bool kv8,
+int launch_paged_decode(const DecodeArgs& a, int B, int head_dim, int gt, bool kv8, bool append,
                         hipStream_t stream) {
   if (B == 0) return 0;
   if (kv8) {
-    if (head_dim == 128) return launch_gt<128, true>(a, B, gt, stream);
-    if (head_dim == 64) return launch_gt<64, true>(a, B, gt, stream);
-  } else {
-    if (head_dim == 128) return launch_gt<128, false>(a, B, gt, stream);
-    if (head_dim == 64) return launch_gt<64, false>(a, B, gt, stream);
+    return append ? launch_head_dim<true, true>(a, B, head_dim, gt, stream)
+                  : launch_head_dim<true, false>(a, B, head_dim, gt, stream);
   }
-  return -2;
+  return append ? launch_head_dim<false, true>(a, B, head_dim, gt, stream)
+                : launch_head_dim<false, false>(a, B, head_dim, gt, stream);
 }
 
 }  // namespace pa

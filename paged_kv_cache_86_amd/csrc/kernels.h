@@ -50,10 +50,18 @@ struct DecodeArgs {
   int mbs, Hq, Hkv, group, nsub, hg, bs_log2, split_log2, nsplit_max, num_blocks, out_f32;
   float scale_log2e;  // softmax scale (times the K scale of an FP8 cache) times log2(e)
   float v_scale;      // V scale of an FP8 cache (1 for bf16)
+  // Fused store of the new token (append variants only; unused otherwise).
+  const uint16_t* k_new;  // [B, Hkv, D] bf16
+  const uint16_t* v_new;
+  const int32_t* slot_mapping;  // [B]
+  void* k_cache_w;  // the caches again, written
+  void* v_cache_w;
+  int64_t num_slots;
+  float qscale_k, qscale_v;  // FP8 quantization divisors
 };
 
 int launch_paged_decode(const DecodeArgs& args, int B, int head_dim, int gt, bool kv8,
-                        hipStream_t stream);
+                        bool append, hipStream_t stream);
 
 int launch_kvcache_store_fp8(const void* k, const void* v, const int32_t* slot_mapping, int T,
                              void* k_cache, void* v_cache, int num_blocks, int block_size,

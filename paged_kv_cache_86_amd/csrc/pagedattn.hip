@@ -79,13 +79,21 @@ size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, i
              : p.workspace_bytes();
 }
 
-// Shared body of the bf16 and FP8 decode entry points.  For FP8 the K scale
-// is folded into the score scale and the V scale multiplies the outputs.
+// The new tokens of a fused store + decode call (all NULL for plain decode).
+struct NewTokens {
+  const void* k;
+  const void* v;
+  const int32_t* slot_mapping;
+};
+
+// Shared body of the decode entry points (bf16 or FP8 pools, with or without
+// the fused store).  For FP8 the K scale is folded into the score scale and
+// the V scale multiplies the outputs.
 int decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
            int max_blocks_per_seq, const int32_t* context_lens, int num_seqs, int num_q_heads,
            int num_kv_heads, int head_dim, int block_size, int num_blocks, float scale,
            bool kv8, float k_scale, float v_scale, void* out, int out_dtype, void* workspace,
-           size_t workspace_bytes, void* stream) {
+           size_t workspace_bytes, void* stream, const NewTokens* append = nullptr) {
   if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
   int bs_log2 = 0;
   const int g = check_geometry(num_kv_heads, head_dim, block_size, num_blocks, &bs_log2);
@@ -97,6 +105,7 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX / 2) return PA_ERR_SHAPE;
   if (num_seqs == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PA_ERR_NULL;
+  if (append && (!append->k || !append->v || !append->slot_mapping)) return PA_ERR_NULL;
   const pa::DecodePlan p = pa::plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                            block_size, max_blocks_per_seq, kv8);
   if (!workspace) return PA_ERR_WORKSPACE;
@@ -130,7 +139,18 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   const float sc = resolve_scale(scale, head_dim);
   a.scale_log2e = (kv8 ? sc * k_scale : sc) * pa::kLog2eHost;
   a.v_scale = kv8 ? v_scale : 1.f;
-  return pa::launch_paged_decode(a, num_seqs, head_dim, p.gt, kv8, (hipStream_t)stream) == 0
+  if (append) {
+    a.k_new = (const uint16_t*)append->k;
+    a.v_new = (const uint16_t*)append->v;
+    a.slot_mapping = append->slot_mapping;
+    a.k_cache_w = (void*)k_cache;
+    a.v_cache_w = (void*)v_cache;
+    a.num_slots = (int64_t)num_blocks * block_size;
+    a.qscale_k = k_scale;
+    a.qscale_v = v_scale;
+  }
+  return pa::launch_paged_decode(a, num_seqs, head_dim, p.gt, kv8, append != nullptr,
+                                 (hipStream_t)stream) == 0
              ? PA_OK
              : PA_ERR_HIP;
 }
@@ -172,6 +192,33 @@ int pa_paged_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
   return decode(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                 num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, true, k_scale,
                 v_scale, out, out_dtype, workspace, workspace_bytes, stream);
+}
+
+int pa_paged_decode_append(const void* q, const void* k_new, const void* v_new,
+                           const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                           const int32_t* block_tables, int max_blocks_per_seq,
+                           const int32_t* context_lens, int num_seqs, int num_q_heads,
+                           int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                           float scale, void* out, int out_dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  const NewTokens nt{k_new, v_new, slot_mapping};
+  return decode(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, false, 1.f,
+                1.f, out, out_dtype, workspace, workspace_bytes, stream, &nt);
+}
+
+int pa_paged_decode_append_fp8(const void* q, const void* k_new, const void* v_new,
+                               const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                               const int32_t* block_tables, int max_blocks_per_seq,
+                               const int32_t* context_lens, int num_seqs, int num_q_heads,
+                               int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                               float scale, float k_scale, float v_scale, void* out,
+                               int out_dtype, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  const NewTokens nt{k_new, v_new, slot_mapping};
+  return decode(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, true, k_scale,
+                v_scale, out, out_dtype, workspace, workspace_bytes, stream, &nt);
 }
 
 int pa_kvcache_store_fp8(const void* k, const void* v, const int32_t* slot_mapping, int T,

@@ -60,32 +60,12 @@ int launch_kvcache_store(const void* k, const void* v, const int32_t* slot_mappi
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-// FP8 store: each thread turns 16 bf16 values of K (and of V) into 16 OCP
-// E4M3 codes: x / scale in fp32 (correctly rounded division), clamped to
-// +-448 so that large magnitudes saturate (the hardware conversion would give
-// NaN from 480 on), NaN kept as S.1111.111, then v_cvt_pk_fp8_f32 (round to
-// nearest even).  Vector e of token t covers elements 16e .. 16e+15 of its row.
-__device__ __forceinline__ uint32_t fp8_code_pair(float x0, float x1, float s) {
-  float q0 = x0 / s, q1 = x1 / s;
-  const bool n0 = q0 != q0, n1 = q1 != q1;
-  q0 = n0 ? 0.f : fminf(fmaxf(q0, -448.f), 448.f);
-  q1 = n1 ? 0.f : fminf(fmaxf(q1, -448.f), 448.f);
-  uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false) & 0xFFFFu;
-  if (n0) c = (c & 0xFF00u) | 0x7Fu | ((__float_as_uint(x0) >> 24) & 0x80u);
-  if (n1) c = (c & 0x00FFu) | 0x7F00u | ((__float_as_uint(x1) >> 16) & 0x8000u);
-  return c;
-}
-
+// FP8 store: each thread turns 16 bf16 values of K (and of V) into 16 E4M3
+// codes (quantize8 twice).  Vector e of token t covers elements 16e .. 16e+15
+// of its row.
 __device__ __forceinline__ u32x4 quantize16(const u32x4& a, const u32x4& b, float s) {
-  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  uint32_t o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t p0 = fp8_code_pair(bf16lo(w[2 * i]), bf16hi(w[2 * i]), s);
-    const uint32_t p1 = fp8_code_pair(bf16lo(w[2 * i + 1]), bf16hi(w[2 * i + 1]), s);
-    o[i] = p0 | (p1 << 16);
-  }
-  return u32x4{o[0], o[1], o[2], o[3]};
+  const u32x2 lo = quantize8(a, s), hi = quantize8(b, s);
+  return u32x4{lo.x, lo.y, hi.x, hi.y};
 }
 
 __global__ __launch_bounds__(256) void kvcache_store_fp8_kernel(

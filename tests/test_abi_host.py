@@ -168,3 +168,21 @@ def test_decode_fp8_workspace_sizes():
     assert pa.decode_workspace_bytes(1, 5, 1, 128, 256, 16) == ws(16 * 5)
     assert pa.decode_fp8_workspace_bytes(1, 5, 1, 128, 256, 16) == ws(16 * 6)
     assert pa.decode_fp8_workspace_bytes(4, 6, 4, 128, 16, 8) == 0
+
+
+def test_decode_append_argument_checks(lib):
+    def app(B=4, Hq=4, Hkv=2, D=128, k_new=FAKE, slots=FAKE, ws_bytes=None, fp8=False):
+        if ws_bytes is None:
+            ws_bytes = pa.decode_workspace_bytes(max(B, 1), Hq, Hkv, D, 16, 8)
+        if fp8:
+            return lib.pa_paged_decode_append_fp8(FAKE, k_new, FAKE, slots, FAKE, FAKE, FAKE, 8,
+                                                  FAKE, B, Hq, Hkv, D, 16, 64, 0.0, 1.0, 0.0,
+                                                  FAKE, 0, FAKE, ws_bytes, None)
+        return lib.pa_paged_decode_append(FAKE, k_new, FAKE, slots, FAKE, FAKE, FAKE, 8, FAKE, B,
+                                          Hq, Hkv, D, 16, 64, 0.0, FAKE, 0, FAKE, ws_bytes, None)
+    assert app(k_new=None) == PA_ERR_NULL
+    assert app(slots=None) == PA_ERR_NULL
+    assert app(B=0, k_new=None) == PA_OK
+    assert app(D=80) == PA_ERR_UNSUPPORTED
+    assert app(ws_bytes=4) == PA_ERR_WORKSPACE
+    assert app(fp8=True) == PA_ERR_SHAPE  # v_scale 0

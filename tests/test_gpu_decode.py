@@ -201,3 +201,51 @@ def test_decode_workspace_shared_by_different_shapes():
         kc, vc = oracle.kvcache_store(c.k_new, c.v_new, c.slot_mapping, c.k_cache, c.v_cache)
         ref = oracle.paged_decode(c.q, kc, vc, c.block_tables, c.context_lens, np.float32(c.scale))
         assert np.abs(got - ref).max() <= ATOL
+
+
+def check_append(c, dev, label, rows=None):
+    """Fused store + decode: caches as after the store (bit-exact), outputs within ATOL."""
+    d = DecodeOnDevice(c, dev)
+    outs = {}
+    for dt in (torch.float32, torch.bfloat16):
+        # the second call appends the same rows again: same slots, same values
+        out = torch.empty((c.batch, c.num_q_heads, c.head_dim), dtype=dt, device=dev)
+        pa.paged_decode_append(d.q, d.k_new, d.v_new, d.slots, d.k_cache, d.v_cache, d.tables,
+                               d.ctx, c.scale, out)
+        outs[dt] = as_f64(out)
+    kc, vc = oracle.kvcache_store(c.k_new, c.v_new, c.slot_mapping, c.k_cache, c.v_cache)
+    assert np.array_equal(bits(d.k_cache), kc) and np.array_equal(bits(d.v_cache), vc)
+    rows = list(range(c.batch)) if rows is None else rows
+    ref = oracle.paged_decode(c.q[rows], kc, vc, c.block_tables[rows], c.context_lens[rows],
+                              np.float32(c.scale))
+    e32 = np.abs(outs[torch.float32][rows] - ref).max()
+    e16 = np.abs(outs[torch.bfloat16][rows] - ref).max()
+    say(f"[append] {label}: max|err| fp32 {e32:.3e} bf16 {e16:.3e} over {len(rows)} seqs")
+    assert e32 <= ATOL and e16 <= ATOL
+    return outs[torch.float32]
+
+
+@pytest.mark.parametrize("cfg_id,limit", [(1, 4), (2, 64), (3, 24), (4, 48)])
+def test_decode_append_workload(cfg_id, limit):
+    dev = device()
+    c = workload(cfg_id)
+    check_append(c, dev, f"workload {cfg_id}", sample_rows(c, limit))
+
+
+APPEND_SMALL = SMALL + [(64, 16, 4, 2, [512, 513, 1025, 1, 0])]
+
+
+@pytest.mark.parametrize("case", APPEND_SMALL,
+                         ids=[f"D{c[0]}_bs{c[1]}_h{c[2]}-{c[3]}" for c in APPEND_SMALL])
+def test_decode_append_small_cases(case):
+    dev = device()
+    D, BS, Hq, Hkv, ctx = case
+    c = decode_case(2468 + D + BS + Hq, ctx, Hq, Hkv, D, BS, nb_factor=1.4)
+    out32 = check_append(c, dev, f"D{D} bs{BS} h{Hq}/{Hkv}")
+    G = Hq // Hkv
+    for i, n in enumerate(ctx):
+        if n == 0:
+            assert np.all(out32[i] == 0)
+        if n == 1:  # the only key is the appended token: out = v_new exactly
+            for h in range(Hq):
+                assert np.array_equal(out32[i, h], oracle.bf16_to_f64(c.v_new[i, h // G]))

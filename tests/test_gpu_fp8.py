@@ -213,3 +213,44 @@ def test_decode_fp8_scales_fold_exactly():
     assert torch.equal(out, base)
     pa.paged_decode_fp8(d.q, d.k_cache, d.v_cache, d.tables, d.ctx, c.scale, d.ks, d.vs * 2, out)
     assert torch.equal(out, base * 2)
+
+
+@pytest.mark.parametrize("case", SMALL[:6] + [(64, 16, 4, 2, [512, 513, 1025, 1, 0])],
+                         ids=lambda c: f"D{c[0]}_bs{c[1]}_h{c[2]}-{c[3]}")
+def test_decode_append_fp8(case):
+    """Fused quantizing store + decode equals store_fp8 then decode_fp8 (caches bit-exact)."""
+    dev = device()
+    D, BS, Hq, Hkv, ctx = case
+    c = decode_case(8642 + D + BS + Hq, ctx, Hq, Hkv, D, BS, nb_factor=1.4)
+    say(f"[fp8-append] D={D} BS={BS} Hq={Hq} Hkv={Hkv} ctx={ctx}")
+    ks, vs = 0.0125, 0.02
+    NB, _, _, _ = c.k_cache.shape
+    kc = torch.empty((NB, BS, Hkv, D), dtype=torch.uint8, device=dev)
+    vc = torch.empty_like(kc)
+    every = np.arange(NB * BS, dtype=np.int32)
+    pa.kvcache_store_fp8(bf16(c.k_cache.reshape(NB * BS, Hkv, D), dev),
+                         bf16(c.v_cache.reshape(NB * BS, Hkv, D), dev), i32(every, dev), kc, vc,
+                         ks, vs)
+    out = torch.empty((c.batch, Hq, D), dtype=torch.float32, device=dev)
+    pa.paged_decode_append_fp8(bf16(c.q, dev), bf16(c.k_new, dev), bf16(c.v_new, dev),
+                               i32(c.slot_mapping, dev), kc, vc, i32(c.block_tables, dev),
+                               i32(c.context_lens, dev), c.scale, ks, vs, out)
+    kc8, vc8 = oracle.kvcache_store_fp8(c.k_new, c.v_new, c.slot_mapping,
+                                        oracle.quantize(c.k_cache, ks),
+                                        oracle.quantize(c.v_cache, vs), ks, vs)
+    assert np.array_equal(codes(kc), kc8) and np.array_equal(codes(vc), vc8)
+    ref = oracle.paged_decode_fp8(c.q, kc8, vc8, c.block_tables, c.context_lens,
+                                  np.float32(c.scale), ks, vs)
+    got = as_f64(out)
+    err = np.abs(got - ref).max()
+    say(f"[fp8-append] max|err| fp32 {err:.3e}")
+    assert err <= ATOL
+    G = Hq // Hkv
+    for i, n in enumerate(ctx):
+        if n == 0:
+            assert np.all(got[i] == 0)
+        if n == 1:
+            blk, off = divmod(int(c.slot_mapping[i]), BS)
+            vrow = np.float32(oracle.e4m3_decode(vc8[blk, off]) * np.float32(vs))
+            for h in range(Hq):
+                assert np.array_equal(got[i, h], vrow[h // G].astype(np.float64))

@@ -196,6 +196,58 @@ int pa_paged_decode_append_fp8(const void* q, const void* k_new, const void* v_n
                                void* stream);
 
 /*
+ * Graph-captured decode steps (MinivLLM guide §4.7: decode steps are captured
+ * once per batch-size bucket 1, 2, 4, 8, 16, 32, ... into static input
+ * buffers, a step fills the first rows, pads the rest with sentinels and
+ * replays the smallest bucket that fits; §4.5: the index tensors are built in
+ * pinned host memory and uploaded with non-blocking copies).
+ *
+ * An opaque object that owns static device buffers (q, new K/V rows, output,
+ * index arrays, split-K workspace), two pinned host staging areas, and one
+ * instantiated HIP graph per bucket of the fused store + decode call
+ * (pa_paged_decode_append, or pa_paged_decode_append_fp8 when kv_fp8 != 0)
+ * over the caller's caches.  Unlike the other calls, create allocates (device
+ * memory, pinned host memory, graphs) and synchronizes the device; run
+ * allocates nothing.
+ *
+ * pa_decode_graph_create: buckets are 1, 2, 4, 8 and the multiples of 16 below
+ *   max_batch (<= 65536), plus max_batch.  k_cache/v_cache must stay valid for
+ *   the object's life.  Other arguments as for the decode calls.
+ * pa_decode_graph_buffers: the static q [max_batch, Hq, D], k_new/v_new
+ *   [max_batch, Hkv, D] (bf16) and out [max_batch, Hq, D] device buffers;
+ *   writing q/k_new/v_new there in place saves run's copies.
+ * pa_decode_graph_bucket: the bucket a batch of `batch` rows replays (0 if
+ *   batch is out of range).
+ * pa_decode_graph_run: one decode step for `batch` sequences on `stream`.
+ *   q, k_new, v_new: device pointers to the batch's rows (copied into the
+ *   static buffers unless they are those buffers; NULL = already there).
+ *   slot_mapping [batch], context_lens [batch] and block_tables
+ *   [batch, tables_stride] (tables_stride <= max_blocks_per_seq) are HOST
+ *   arrays: they are copied into pinned staging (rows batch..bucket-1 get
+ *   slot -1, length 0 and table -1) and uploaded asynchronously; the host
+ *   blocks only if the staging area it is about to refill is still being
+ *   uploaded by the step before last.  out: device pointer that receives the
+ *   batch's rows (NULL = leave them in the static output).  Must be called on
+ *   the device the object was created on; consecutive runs of one object
+ *   must use the same stream (or be ordered by the caller).
+ * pa_decode_graph_destroy: waits for the device, frees everything.  NULL is a no-op.
+ */
+typedef struct pa_decode_graph pa_decode_graph;
+
+int pa_decode_graph_create(int max_batch, int num_q_heads, int num_kv_heads, int head_dim,
+                           int block_size, int num_blocks, int max_blocks_per_seq, int kv_fp8,
+                           float scale, float k_scale, float v_scale, void* k_cache,
+                           void* v_cache, int out_dtype, pa_decode_graph** out_graph);
+int pa_decode_graph_buffers(const pa_decode_graph* graph, void** q, void** k_new, void** v_new,
+                            void** out);
+int pa_decode_graph_bucket(const pa_decode_graph* graph, int batch);
+int pa_decode_graph_run(pa_decode_graph* graph, int batch, const void* q, const void* k_new,
+                        const void* v_new, const int32_t* slot_mapping,
+                        const int32_t* block_tables, int tables_stride,
+                        const int32_t* context_lens, void* out, void* stream);
+int pa_decode_graph_destroy(pa_decode_graph* graph);
+
+/*
  * Prefix-hit prefill ("Nano-vLLM源码学习(2)" §2: the prefix-hit prefill path
  * reads the cached prefix through block_table; MinivLLM guide §4.5: the batch
  * is flattened and delimited by cu_seqlens_q, e.g. [0, 3, 5, 9]).

@@ -35,6 +35,11 @@ EXPORTED_SYMBOLS = (
     "pa_paged_decode_fp8",
     "pa_paged_decode_append",
     "pa_paged_decode_append_fp8",
+    "pa_decode_graph_create",
+    "pa_decode_graph_buffers",
+    "pa_decode_graph_bucket",
+    "pa_decode_graph_run",
+    "pa_decode_graph_destroy",
 )
 
 _lib = None
@@ -82,6 +87,17 @@ def load_library() -> ctypes.CDLL:
     lib.pa_paged_decode_append_fp8.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, F,
                                                F, F, P, I, P, Z, P]
     lib.pa_paged_decode_append_fp8.restype = I
+    PP = ctypes.POINTER(ctypes.c_void_p)
+    lib.pa_decode_graph_create.argtypes = [I, I, I, I, I, I, I, I, F, F, F, P, P, I, PP]
+    lib.pa_decode_graph_create.restype = I
+    lib.pa_decode_graph_buffers.argtypes = [P, PP, PP, PP, PP]
+    lib.pa_decode_graph_buffers.restype = I
+    lib.pa_decode_graph_bucket.argtypes = [P, I]
+    lib.pa_decode_graph_bucket.restype = I
+    lib.pa_decode_graph_run.argtypes = [P, I, P, P, P, P, P, I, P, P, P]
+    lib.pa_decode_graph_run.restype = I
+    lib.pa_decode_graph_destroy.argtypes = [P]
+    lib.pa_decode_graph_destroy.restype = I
     _lib = lib
     return lib
 
@@ -358,3 +374,99 @@ def paged_decode_append_fp8(q, k_new, v_new, slot_mapping, k_cache, v_cache, blo
         float(v_scale), _ptr(out), _out_dtype(out), _ptr(workspace), int(workspace.numel()),
         _stream(q.device))
     _raise_on("pa_paged_decode_append_fp8", rc)
+
+
+class DecodeGraph:
+    """Graph-captured fused store + decode steps over fixed caches, one graph per batch bucket.
+
+    ``run`` takes the step's q / k_new / v_new as device tensors (or None when they were
+    written into :attr:`q`, :attr:`k_new`, :attr:`v_new` in place) and the index arrays as
+    host (CPU) int32 tensors or arrays; rows past the batch are padded with sentinels.
+    """
+
+    def __init__(self, k_cache, v_cache, max_batch: int, num_q_heads: int,
+                 max_blocks_per_seq: int, scale: Optional[float] = None, *,
+                 k_scale: Optional[float] = None, v_scale: Optional[float] = None,
+                 out_dtype=None):
+        torch = _torch()
+        fp8 = k_cache.dtype == torch.uint8
+        if fp8 and (k_scale is None or v_scale is None):
+            raise ValueError("an FP8 cache needs k_scale and v_scale")
+        NB, BS, Hkv, D = _cache_geometry(k_cache, v_cache, k_cache.dtype if fp8 else None)
+        out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+        self._lib = load_library()
+        self._caches = (k_cache, v_cache)  # keep the pools alive
+        self.device = k_cache.device
+        self.max_batch, self.num_q_heads, self.num_kv_heads, self.head_dim = (
+            int(max_batch), int(num_q_heads), Hkv, D)
+        self.out_dtype = out_dtype
+        handle = ctypes.c_void_p()
+        with torch.cuda.device(self.device):
+            rc = self._lib.pa_decode_graph_create(
+                int(max_batch), int(num_q_heads), Hkv, D, BS, NB, int(max_blocks_per_seq),
+                1 if fp8 else 0, float(scale) if scale is not None else 0.0,
+                float(k_scale) if fp8 else 1.0, float(v_scale) if fp8 else 1.0,
+                _ptr(k_cache), _ptr(v_cache), PA_F32 if out_dtype == torch.float32 else PA_BF16,
+                ctypes.byref(handle))
+        _raise_on("pa_decode_graph_create", rc)
+        self._h = handle
+        ptrs = [ctypes.c_void_p() for _ in range(4)]
+        _raise_on("pa_decode_graph_buffers", self._lib.pa_decode_graph_buffers(
+            self._h, *[ctypes.byref(p) for p in ptrs]))
+        self._buf_ptrs = [p.value for p in ptrs]
+
+    def bucket(self, batch: int) -> int:
+        return int(self._lib.pa_decode_graph_bucket(self._h, int(batch)))
+
+    def buffer_ptrs(self):
+        """Device addresses of the static q, k_new, v_new and out buffers."""
+        return tuple(self._buf_ptrs)
+
+    def run(self, batch: int, q, k_new, v_new, slot_mapping, block_tables, context_lens,
+            out=None) -> None:
+        import numpy as np
+        torch = _torch()
+
+        def host_i32(a, name, ndim):
+            a = a.numpy() if isinstance(a, torch.Tensor) else a
+            a = np.ascontiguousarray(a, dtype=np.int32)
+            if a.ndim != ndim:
+                raise ValueError(f"{name} must have {ndim} dims")
+            return a
+
+        B = int(batch)
+        sl = host_i32(slot_mapping, "slot_mapping", 1)
+        bt = host_i32(block_tables, "block_tables", 2)
+        cl = host_i32(context_lens, "context_lens", 1)
+        if sl.shape[0] < B or cl.shape[0] < B or bt.shape[0] < B:
+            raise ValueError("index arrays need one row per sequence")
+        for t, name, rows, heads in ((q, "q", B, self.num_q_heads), (k_new, "k_new", B, self.num_kv_heads),
+                                     (v_new, "v_new", B, self.num_kv_heads)):
+            if t is not None:
+                _check(t, torch.bfloat16, name, 3)
+                if tuple(t.shape) != (rows, heads, self.head_dim):
+                    raise ValueError(f"{name} must be [{rows}, {heads}, {self.head_dim}]")
+        if out is not None:
+            _check(out, self.out_dtype, "out", 3)
+            if tuple(out.shape) != (B, self.num_q_heads, self.head_dim):
+                raise ValueError("out shape")
+
+        def p(t):
+            return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+        rc = self._lib.pa_decode_graph_run(
+            self._h, B, p(q), p(k_new), p(v_new), sl.ctypes.data_as(ctypes.c_void_p),
+            bt.ctypes.data_as(ctypes.c_void_p), int(bt.shape[1]), cl.ctypes.data_as(ctypes.c_void_p),
+            p(out), _stream(self.device))
+        _raise_on("pa_decode_graph_run", rc)
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._lib.pa_decode_graph_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpagedattn.so")
-SOURCES = ["pagedattn.hip", "store_gather.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["pagedattn.hip", "store_gather.hip", "decode.hip", "prefill.hip", "graph.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -186,3 +186,22 @@ def test_decode_append_argument_checks(lib):
     assert app(D=80) == PA_ERR_UNSUPPORTED
     assert app(ws_bytes=4) == PA_ERR_WORKSPACE
     assert app(fp8=True) == PA_ERR_SHAPE  # v_scale 0
+
+
+def test_decode_graph_argument_checks(lib):
+    h = ctypes.c_void_p()
+
+    def create(max_batch=8, Hq=4, Hkv=2, D=128, out_dtype=0, kc=FAKE, handle=True):
+        return lib.pa_decode_graph_create(max_batch, Hq, Hkv, D, 16, 64, 8, 0, 0.0, 1.0, 1.0, kc,
+                                          FAKE, out_dtype, ctypes.byref(h) if handle else None)
+    assert create(handle=False) == PA_ERR_NULL
+    assert create(max_batch=0) == PA_ERR_SHAPE
+    assert create(max_batch=70000) == PA_ERR_SHAPE
+    assert create(kc=None) == PA_ERR_NULL
+    assert create(out_dtype=3) == PA_ERR_UNSUPPORTED
+    assert create(Hq=6, Hkv=4) == PA_ERR_SHAPE  # no workspace size for these heads
+    assert h.value is None
+    assert lib.pa_decode_graph_run(None, 1, None, None, None, None, None, 1, None, None,
+                                   None) == PA_ERR_NULL
+    assert lib.pa_decode_graph_bucket(None, 3) == 0
+    assert lib.pa_decode_graph_destroy(None) == PA_OK

@@ -1,0 +1,131 @@
+"""Graph-captured decode steps: every replay equals the eager fused store + decode call, bit for
+bit (outputs and caches), across batch buckets with padded rows, with eager work between replays
+and with back-to-back steps that reuse the pinned staging."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_86_amd as pa
+from gpu_util import bf16, bits, device, i32, say
+from workloads import decode_case
+
+pytestmark = pytest.mark.gpu
+
+
+def same_bits(a, b):
+    """Bitwise equality (the pools hold NaN in unused slots, and NaN != NaN)."""
+    return torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def make_case(seed, B, D=128, BS=16, Hq=16, Hkv=8, max_ctx=700):
+    ctx = np.random.default_rng(seed).integers(1, max_ctx, size=B)
+    ctx[::7] = 0  # padded rows inside the batch as well
+    return decode_case(seed, ctx, Hq, Hkv, D, BS, nb_factor=1.3,
+                       max_blocks_per_seq=-(-max_ctx // BS))
+
+
+def eager_step(c, rows, kc, vc, dev, out_dtype):
+    out = torch.empty((len(rows), c.num_q_heads, c.head_dim), dtype=out_dtype, device=dev)
+    pa.paged_decode_append(bf16(c.q[rows], dev), bf16(c.k_new[rows], dev), bf16(c.v_new[rows], dev),
+                           i32(c.slot_mapping[rows], dev), kc, vc, i32(c.block_tables[rows], dev),
+                           i32(c.context_lens[rows], dev), c.scale, out)
+    return out
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_graph_replays_equal_eager(out_dtype):
+    dev = device()
+    c = make_case(501, 64)
+    kc_g, vc_g = bf16(c.k_cache, dev), bf16(c.v_cache, dev)
+    kc_e, vc_e = bf16(c.k_cache, dev), bf16(c.v_cache, dev)
+    g = pa.DecodeGraph(kc_g, vc_g, 64, c.num_q_heads, c.max_blocks_per_seq, c.scale,
+                       out_dtype=out_dtype)
+    assert [g.bucket(b) for b in (1, 2, 3, 5, 9, 16, 17, 33, 63, 64)] == \
+        [1, 2, 4, 8, 16, 16, 32, 48, 64, 64]
+    assert g.bucket(0) == 0 and g.bucket(65) == 0
+    rng = np.random.default_rng(502)
+    for rep, B in enumerate([1, 3, 16, 17, 40, 64, 5, 64]):
+        rows = np.sort(rng.choice(c.batch, B, replace=False))
+        say(f"[graph] replay {rep}: batch {B} -> bucket {g.bucket(B)}")
+        out_g = torch.full((B, c.num_q_heads, c.head_dim), float("nan"), dtype=out_dtype, device=dev)
+        g.run(B, bf16(c.q[rows], dev), bf16(c.k_new[rows], dev), bf16(c.v_new[rows], dev),
+              c.slot_mapping[rows], c.block_tables[rows], c.context_lens[rows], out=out_g)
+        torch.cuda.synchronize()
+        out_e = eager_step(c, rows, kc_e, vc_e, dev, out_dtype)
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e)
+        assert same_bits(kc_g, kc_e) and same_bits(vc_g, vc_e)
+        # eager work of the program between replays
+        junk = torch.randn(1 << 20, device=dev)
+        (junk * 2).sum().item()
+    g.close()
+
+
+def test_graph_back_to_back_steps_and_static_buffers():
+    """Steps issued without host synchronization keep their own index data; a step whose
+    q/k/v are already in the static buffers passes None and copies nothing."""
+    dev = device()
+    c = make_case(503, 48, D=64, BS=32, Hq=8, Hkv=2)
+    kc_g, vc_g = bf16(c.k_cache, dev), bf16(c.v_cache, dev)
+    kc_e, vc_e = bf16(c.k_cache, dev), bf16(c.v_cache, dev)
+    g = pa.DecodeGraph(kc_g, vc_g, 48, c.num_q_heads, c.max_blocks_per_seq, None,
+                       out_dtype=torch.float32)
+    splits = [np.arange(0, 10), np.arange(10, 33), np.arange(33, 48), np.arange(5, 20)]
+    outs = []
+    for rows in splits:
+        o = torch.empty((len(rows), c.num_q_heads, c.head_dim), dtype=torch.float32, device=dev)
+        g.run(len(rows), bf16(c.q[rows], dev), bf16(c.k_new[rows], dev), bf16(c.v_new[rows], dev),
+              c.slot_mapping[rows], c.block_tables[rows], c.context_lens[rows], out=o)
+        outs.append(o)
+    torch.cuda.synchronize()
+    for rows, o in zip(splits, outs):
+        e = eager_step(c, rows, kc_e, vc_e, dev, torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(o, e)
+    # the previous step's inputs stay in the static buffers: a step with no q/k/v copies
+    rows = np.arange(0, 48)
+    B = len(rows)
+    g.run(B, bf16(c.q[rows], dev), bf16(c.k_new[rows], dev), bf16(c.v_new[rows], dev), c.slot_mapping[rows],
+          c.block_tables[rows], c.context_lens[rows])
+    o2 = torch.empty((B, c.num_q_heads, c.head_dim), dtype=torch.float32, device=dev)
+    g.run(B, None, None, None, c.slot_mapping[rows], c.block_tables[rows], c.context_lens[rows],
+          out=o2)
+    torch.cuda.synchronize()
+    e = eager_step(c, rows, kc_e, vc_e, dev, torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, e)
+    g.close()
+
+
+def test_graph_fp8_cache():
+    dev = device()
+    c = make_case(504, 32)
+    NB, BS, Hkv, D = c.k_cache.shape
+    ks, vs = 0.0125, 0.02
+
+    def fp8_pools():
+        k8 = torch.empty((NB, BS, Hkv, D), dtype=torch.uint8, device=dev)
+        v8 = torch.empty_like(k8)
+        every = np.arange(NB * BS, dtype=np.int32)
+        pa.kvcache_store_fp8(bf16(c.k_cache.reshape(NB * BS, Hkv, D), dev),
+                             bf16(c.v_cache.reshape(NB * BS, Hkv, D), dev), i32(every, dev),
+                             k8, v8, ks, vs)
+        return k8, v8
+    kg, vg = fp8_pools()
+    ke, ve = fp8_pools()
+    g = pa.DecodeGraph(kg, vg, 32, c.num_q_heads, c.max_blocks_per_seq, c.scale, k_scale=ks,
+                       v_scale=vs, out_dtype=torch.float32)
+    for B in (7, 32, 1):
+        rows = np.arange(B)
+        o = torch.empty((B, c.num_q_heads, D), dtype=torch.float32, device=dev)
+        g.run(B, bf16(c.q[rows], dev), bf16(c.k_new[rows], dev), bf16(c.v_new[rows], dev),
+              c.slot_mapping[rows], c.block_tables[rows], c.context_lens[rows], out=o)
+        e = torch.empty_like(o)
+        pa.paged_decode_append_fp8(bf16(c.q[rows], dev), bf16(c.k_new[rows], dev),
+                                   bf16(c.v_new[rows], dev), i32(c.slot_mapping[rows], dev), ke, ve,
+                                   i32(c.block_tables[rows], dev), i32(c.context_lens[rows], dev),
+                                   c.scale, ks, vs, e)
+        torch.cuda.synchronize()
+        assert torch.equal(o, e)
+        assert torch.equal(kg, ke) and torch.equal(vg, ve)
+    g.close()

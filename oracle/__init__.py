@@ -11,6 +11,7 @@ Every function is pinned by ``tests/test_oracle.py`` (closed forms, brute
 force on tiny inputs, a library attention routine, permutation invariance and
 the pages' worked examples); there is no "parity unpinned" function here.
 """
+from .block_manager import BlockManager, block_hash, fnv1a64  # noqa: F401
 from .fp8 import (  # noqa: F401
     E4M3_MAX,
     dequantize,

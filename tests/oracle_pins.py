@@ -439,4 +439,155 @@ def pin_fp8_store_writes_exactly_mapped_slots():
             assert np.array_equal(vc[b, o], base[b, o] if t is None else vq[t])
 
 
+# --------------------------------------------------------------------------- block manager
+
+def pin_fnv1a_published_vectors():
+    """64-bit FNV-1a test vectors published with the algorithm."""
+    from oracle import fnv1a64
+    assert fnv1a64(b"") == 0xCBF29CE484222325
+    assert fnv1a64(b"a") == 0xAF63DC4C8601EC8C
+    assert fnv1a64(b"foobar") == 0x85944171F73967E8
+
+
+def pin_block_hash_bytes():
+    """The chained block hash is FNV-1a of the predecessor's hash then the token ids, LE."""
+    from oracle import block_hash, fnv1a64
+    toks = [1, 2, 3, 70000]
+    first = b"".join(t.to_bytes(4, "little") for t in toks)
+    assert block_hash(toks, -1) == fnv1a64(first)
+    prev = 0x0123456789ABCDEF
+    assert block_hash(toks, prev) == fnv1a64(prev.to_bytes(8, "little") + first)
+    assert block_hash(toks, prev, 5) == fnv1a64(prev.to_bytes(8, "little") + first) & 31
+    # the same tokens under another prefix hash differently (the pages' [prefix1][1,2,3] example)
+    assert block_hash([1, 2, 3], 11) != block_hash([1, 2, 3], 12)
+
+
+def pin_block_manager_boundary_example():
+    """The 257th token of a sequence with one full 256-token block opens a new block at offset 0
+    (the pages' prepare_decode example, stored in tests/golden/slot_block_boundary.json)."""
+    g = json.load(open(os.path.join(GOLDEN, "slot_block_boundary.json")))
+    bs = g["block_size"]
+    bm = oracle.BlockManager(8, bs)
+    bm.allocate(1, list(range(g["tokens_before"])))
+    assert len(bm.block_table(1)) == 1
+    bm.append(1, 99)
+    t = bm.block_table(1)
+    assert len(t) == 2
+    assert bm.decode_slot(1) == t[1] * bs + g["expected_offset"]
+    # a sequence's own tokens before the boundary stay in its first block
+    assert bm.prefill_slots(1)[g["tokens_before"] - 1] == t[0] * bs + bs - 1
+
+
+def pin_block_manager_prefix_sharing():
+    """Two prompts with the same two full blocks share their physical blocks (ref count 2) and
+    the second sees 2*BS cached tokens; the partial tails are private."""
+    bs = 4
+    bm = oracle.BlockManager(16, bs)
+    a = [5, 6, 7, 8, 9, 10, 11, 12, 1, 2]
+    b = [5, 6, 7, 8, 9, 10, 11, 12, 3]
+    assert bm.allocate(1, a) == 0
+    assert bm.allocate(2, b) == 2 * bs
+    ta, tb = bm.block_table(1), bm.block_table(2)
+    assert ta[:2] == tb[:2] and ta[2] != tb[2]
+    assert [bm.blocks[x].ref_count for x in ta] == [2, 2, 1]
+    assert bm.prefill_slots(2) == [tb[2] * bs + 0]
+    assert len(bm.free) == 16 - 4
+    # a prompt that is a strict prefix shares only full blocks
+    assert bm.allocate(3, a[:6]) == bs
+    assert bm.block_table(3)[0] == ta[0] and bm.block_table(3)[1] not in ta
+
+
+def pin_block_manager_chained_hash_blocks_false_reuse():
+    """A block with the same tokens after a different first block is not reused."""
+    bs = 3
+    bm = oracle.BlockManager(10, bs)
+    bm.allocate(1, [1, 2, 3, 7, 8, 9])
+    assert bm.allocate(2, [4, 5, 6, 7, 8, 9]) == 0
+    assert set(bm.block_table(1)).isdisjoint(bm.block_table(2))
+
+
+def pin_block_manager_cache_survives_free():
+    """Freed blocks stay findable: the same prompt again hits every full block, and the freed
+    blocks come back off the free list; deallocation frees the last block first."""
+    bs = 4
+    bm = oracle.BlockManager(8, bs)
+    toks = list(range(100, 111))  # 2 full blocks + 3 tokens
+    bm.allocate(1, toks)
+    t1 = bm.block_table(1)
+    bm.deallocate(1)
+    assert list(bm.free)[-3:] == t1[::-1]
+    assert bm.allocate(2, toks) == 2 * bs
+    t2 = bm.block_table(2)
+    assert t2[:2] == t1[:2]
+    assert all(bm.blocks[x].ref_count == 1 for x in t2)
+    assert len(bm.free) == 8 - 3
+
+
+def pin_block_manager_append_hashes_full_blocks():
+    """Decode appends fill the last block; once full it is hashed and a new prompt with the
+    same tokens hits it."""
+    bs = 4
+    bm = oracle.BlockManager(8, bs)
+    bm.allocate(1, [1, 2])
+    for t in (3, 4, 5):
+        assert bm.can_append(1)
+        bm.append(1, t)
+    assert len(bm.block_table(1)) == 2
+    assert bm.allocate(2, [1, 2, 3, 4, 9]) == bs
+    assert bm.block_table(2)[0] == bm.block_table(1)[0]
+
+
+def _bm_check_invariants(bm):
+    n = len(bm.blocks)
+    free = list(bm.free)
+    assert len(set(free)) == len(free)
+    assert set(free).isdisjoint(bm.used) and set(free) | bm.used == set(range(n))
+    counts = {}
+    for sq in bm.seqs.values():
+        for x in sq.block_table:
+            counts[x] = counts.get(x, 0) + 1
+        bs = bm.block_size
+        assert len(sq.block_table) == -(-len(sq.token_ids) // bs)
+        for i, x in enumerate(sq.block_table):
+            toks = sq.token_ids[i * bs:(i + 1) * bs]
+            if len(toks) == bs:  # a full block holds exactly this sequence's tokens
+                assert bm.blocks[x].token_ids == toks
+        if sq.token_ids:
+            p = len(sq.token_ids) - 1
+            assert bm.decode_slot(sq.seq_id) == sq.block_table[p // bs] * bs + p % bs
+    for x in range(n):
+        assert bm.blocks[x].ref_count == counts.get(x, 0)
+    # slots of partial (last, unfilled) blocks belong to one sequence only
+    partial = [sq.block_table[-1] for sq in bm.seqs.values()
+               if sq.token_ids and len(sq.token_ids) % bm.block_size]
+    assert len(partial) == len(set(partial))
+
+
+def pin_block_manager_random_invariants():
+    """Random allocate / append / deallocate runs keep the books straight, also with a 3-bit
+    hash where collisions are frequent (the token compare keeps distinct contents apart)."""
+    for hash_bits, seed in ((64, 40), (3, 41), (1, 42)):
+        rng = np.random.default_rng(seed)
+        bm = oracle.BlockManager(40, 4, hash_bits)
+        prompts = [list(rng.integers(0, 3, size=12)) for _ in range(4)]
+        live = []
+        for step in range(400):
+            op = rng.integers(0, 3)
+            if op == 0 and len(live) < 8:
+                base = prompts[rng.integers(0, len(prompts))]
+                toks = base[:rng.integers(1, 13)] + list(rng.integers(0, 3, size=rng.integers(0, 6)))
+                if bm.can_allocate(len(toks)):
+                    sid = 1000 + step
+                    bm.allocate(sid, toks)
+                    live.append(sid)
+            elif op == 1 and live:
+                sid = live[rng.integers(0, len(live))]
+                if bm.can_append(sid):
+                    bm.append(sid, int(rng.integers(0, 3)))
+            elif op == 2 and live:
+                sid = live.pop(rng.integers(0, len(live)))
+                bm.deallocate(sid)
+            _bm_check_invariants(bm)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

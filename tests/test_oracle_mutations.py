@@ -3,13 +3,16 @@ import numpy as np
 import pytest
 
 import oracle
+import oracle.block_manager as bm_oracle
 import oracle.fp8 as fp8_oracle
 import oracle.paged_attention as pa_oracle
 from oracle_pins import PINS
 
 
 def _caught(monkeypatch, name, replacement):
-    for mod in (pa_oracle, fp8_oracle, oracle):
+    if name.startswith("BlockManager."):
+        monkeypatch.setattr(bm_oracle.BlockManager, name.split(".", 1)[1], replacement)
+    for mod in (pa_oracle, fp8_oracle, bm_oracle, oracle):
         if hasattr(mod, name):
             monkeypatch.setattr(mod, name, replacement)
     failed = []
@@ -95,7 +98,69 @@ def _encode_truncate(x):
     lo = np.clip(np.searchsorted(vals, np.minimum(a, 448.0), side="right") - 1, 0, 0x7E)
     return (lo.astype(np.uint8) | (np.signbit(x).astype(np.uint8) << 7)).astype(np.uint8)
 
+ORIGINAL_HASH = bm_oracle.block_hash
+ORIGINAL_ALLOCATE = bm_oracle.BlockManager.allocate
+ORIGINAL_APPEND = bm_oracle.BlockManager.append
+ORIGINAL_DEALLOCATE = bm_oracle.BlockManager.deallocate
+
+
+def _fnv_wrong_prime(data, h=bm_oracle.FNV_OFFSET):
+    for b in data:
+        h = ((h ^ b) * 0x100000001B5) & bm_oracle.MASK64
+    return h
+
+
+class _Loose(list):
+    """A token list that never differs from another: the cache-miss token compare always passes."""
+
+    def __ne__(self, other):
+        return False
+
+
+def _allocate_without_token_compare(self, seq_id, tokens):
+    for blk in self.blocks:
+        blk.token_ids = _Loose(blk.token_ids)
+    try:
+        return ORIGINAL_ALLOCATE(self, seq_id, tokens)
+    finally:
+        for blk in self.blocks:
+            blk.token_ids = list(blk.token_ids)
+
+
+def _allocate_no_ref_on_hit(self, seq_id, tokens):
+    before = [b.ref_count for b in self.blocks]
+    n = ORIGINAL_ALLOCATE(self, seq_id, tokens)
+    for b, r in zip(self.blocks, before):
+        if r > 0 and b.ref_count == r + 1:
+            b.ref_count = r
+    return n
+
+
+def _append_opens_late(self, seq_id, token):
+    seq = self.seqs[seq_id]
+    seq.token_ids.append(int(token))
+    n, bs = len(seq.token_ids), self.block_size
+    if n % bs == 0 and n // bs >= len(seq.block_table):
+        seq.block_table.append(self._take(self.free[0]).block_id)
+
+
+def _deallocate_first_block_first(self, seq_id):
+    seq = self.seqs.pop(seq_id)
+    for bid in seq.block_table:
+        blk = self.blocks[bid]
+        blk.ref_count -= 1
+        if blk.ref_count == 0:
+            self.used.discard(bid)
+            self.free.append(bid)
+
+
 MUTATIONS = {
+    "bm_hash_wrong_prime": ("fnv1a64", _fnv_wrong_prime),
+    "bm_hash_ignores_prefix": ("block_hash", lambda t, p, b=64: ORIGINAL_HASH(t, -1, b)),
+    "bm_no_token_compare": ("BlockManager.allocate", _allocate_without_token_compare),
+    "bm_no_ref_on_hit": ("BlockManager.allocate", _allocate_no_ref_on_hit),
+    "bm_append_opens_late": ("BlockManager.append", _append_opens_late),
+    "bm_free_first_block_first": ("BlockManager.deallocate", _deallocate_first_block_first),
     "gqa_modulo": ("kv_head_for", lambda h, g: h % max(1, g) if g > 1 else h // g),
     "causal_excludes_self": ("visible", lambda t, j, P: j < P + t),
     "causal_ignores_prefix": ("visible", lambda t, j, P: j <= t + 0 * P),

@@ -61,7 +61,9 @@ typedef enum {
   PA_ERR_SHAPE = -2,       /* a size is negative/zero where it may not be, or inconsistent */
   PA_ERR_UNSUPPORTED = -3, /* head_dim / block_size / dtype outside the supported set */
   PA_ERR_WORKSPACE = -4,   /* decode workspace missing or too small */
-  PA_ERR_HIP = -5          /* a kernel launch failed */
+  PA_ERR_HIP = -5,         /* a kernel launch (or another HIP call) failed */
+  PA_ERR_OUT_OF_BLOCKS = -6, /* block manager: not enough free blocks */
+  PA_ERR_SEQUENCE = -7     /* block manager: unknown (or already allocated) sequence id */
 } pa_status;
 
 typedef enum { PA_BF16 = 0, PA_F32 = 1 } pa_dtype; /* output element type */
@@ -282,6 +284,75 @@ int pa_paged_gather(const void* cache, const int32_t* block_tables, int max_bloc
                     const int32_t* context_lens, const int32_t* cu_seqlens_k, int num_seqs,
                     int max_context_len, int num_kv_heads, int head_dim, int block_size,
                     int num_blocks, void* out, void* stream);
+
+/*
+ * Host block manager with prefix caching (MinivLLM guide Step 3 §3.2 Block,
+ * §3.3 BlockManager; Step 4 §4.5 prepare_prefill / prepare_decode).  Host
+ * memory only, no GPU calls; not thread-safe (one caller at a time per
+ * object).  It hands out the physical block ids of one KV pool and produces
+ * the slot_mapping / block_tables / context_lens / cu_seqlens_q arrays the
+ * kernels above consume.
+ *
+ * Readings where the pages leave a step open:
+ * - A full block's hash is 64-bit FNV-1a over the previous block's hash (8
+ *   bytes, little endian; omitted for the first block) then the block's token
+ *   ids (4 bytes each, little endian), masked to hash_bits bits (64 = all;
+ *   fewer only to provoke collisions in tests).  A cached block is reused only
+ *   if its hash is registered and it holds exactly the same tokens.
+ * - Free blocks form a FIFO list, initially 0..num_blocks-1: allocation takes
+ *   the head, a freed block joins the tail and keeps its contents and hash
+ *   (still reusable) until it is handed out for other contents.
+ * - allocate: the prompt's blocks in order; the first miss makes every later
+ *   block a miss; a hit on a block in use adds a reference, a hit on a free
+ *   block takes it back (reference count 1); a missed full block gets a fresh
+ *   block and registers its hash; the partial last block is never shared.
+ *   can_allocate counts all the prompt's blocks (hits not subtracted).
+ * - append adds one token: it takes a new block when the token opens one and
+ *   registers the last block's hash when the token fills it (a 256-token
+ *   sequence's 257th token opens block 2 at offset 0).
+ * - deallocate drops one reference per table entry, last block first; blocks
+ *   reaching zero join the free list in that order.
+ *
+ * pa_bm_create: num_blocks * block_size <= INT32_MAX, 1 <= hash_bits <= 64.
+ * pa_bm_can_allocate / pa_bm_can_append return 1 or 0 (or an error < 0).
+ * pa_bm_allocate: *num_cached_tokens = tokens covered by reused blocks.
+ *   PA_ERR_OUT_OF_BLOCKS if can_allocate is false (nothing changes);
+ *   PA_ERR_SEQUENCE if seq_id is live.
+ * pa_bm_append: PA_ERR_OUT_OF_BLOCKS (nothing changes) if the token needs a
+ *   block and none is free.
+ * pa_bm_block_table / pa_bm_free_list: write up to `capacity` entries, return
+ *   the full count.  pa_bm_ref_count: a block's reference count.
+ * pa_bm_prepare_decode: per sequence, context_lens = its length, slot_mapping =
+ *   slot of its last token, block_tables row padded with -1 to
+ *   max_blocks_per_seq (PA_ERR_SHAPE if a table is longer).
+ * pa_bm_prepare_prefill: per sequence, its uncached tokens (positions
+ *   num_cached .. len-1): cu_seqlens_q [num_seqs+1] over those counts,
+ *   slot_mapping [total_q] (at most slot_capacity), context_lens = lengths,
+ *   padded block_tables; *total_q and *max_q_len for the prefill call.
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+int pa_bm_create(int num_blocks, int block_size, int hash_bits, pa_block_manager** out);
+int pa_bm_destroy(pa_block_manager* bm);
+int pa_bm_num_free(const pa_block_manager* bm);
+int pa_bm_can_allocate(const pa_block_manager* bm, int num_tokens);
+int pa_bm_allocate(pa_block_manager* bm, int64_t seq_id, const int32_t* tokens, int num_tokens,
+                   int* num_cached_tokens);
+int pa_bm_can_append(const pa_block_manager* bm, int64_t seq_id);
+int pa_bm_append(pa_block_manager* bm, int64_t seq_id, int32_t token);
+int pa_bm_deallocate(pa_block_manager* bm, int64_t seq_id);
+int pa_bm_seq_info(const pa_block_manager* bm, int64_t seq_id, int* num_tokens,
+                   int* num_cached_tokens, int* num_blocks);
+int pa_bm_block_table(const pa_block_manager* bm, int64_t seq_id, int32_t* out, int capacity);
+int pa_bm_free_list(const pa_block_manager* bm, int32_t* out, int capacity);
+int pa_bm_ref_count(const pa_block_manager* bm, int block_id);
+int pa_bm_prepare_decode(const pa_block_manager* bm, const int64_t* seq_ids, int num_seqs,
+                         int max_blocks_per_seq, int32_t* slot_mapping, int32_t* context_lens,
+                         int32_t* block_tables);
+int pa_bm_prepare_prefill(const pa_block_manager* bm, const int64_t* seq_ids, int num_seqs,
+                          int max_blocks_per_seq, int32_t* cu_seqlens_q, int32_t* context_lens,
+                          int32_t* block_tables, int32_t* slot_mapping, int slot_capacity,
+                          int* total_q, int* max_q_len);
 
 #ifdef __cplusplus
 }

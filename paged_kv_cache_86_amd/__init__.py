@@ -40,6 +40,20 @@ EXPORTED_SYMBOLS = (
     "pa_decode_graph_bucket",
     "pa_decode_graph_run",
     "pa_decode_graph_destroy",
+    "pa_bm_create",
+    "pa_bm_destroy",
+    "pa_bm_num_free",
+    "pa_bm_can_allocate",
+    "pa_bm_allocate",
+    "pa_bm_can_append",
+    "pa_bm_append",
+    "pa_bm_deallocate",
+    "pa_bm_seq_info",
+    "pa_bm_block_table",
+    "pa_bm_free_list",
+    "pa_bm_ref_count",
+    "pa_bm_prepare_decode",
+    "pa_bm_prepare_prefill",
 )
 
 _lib = None
@@ -98,6 +112,19 @@ def load_library() -> ctypes.CDLL:
     lib.pa_decode_graph_run.restype = I
     lib.pa_decode_graph_destroy.argtypes = [P]
     lib.pa_decode_graph_destroy.restype = I
+    L, IP = ctypes.c_int64, ctypes.POINTER(ctypes.c_int)
+    bm_sigs = {
+        "pa_bm_create": [I, I, I, PP], "pa_bm_destroy": [P], "pa_bm_num_free": [P],
+        "pa_bm_can_allocate": [P, I], "pa_bm_allocate": [P, L, P, I, IP],
+        "pa_bm_can_append": [P, L], "pa_bm_append": [P, L, ctypes.c_int32],
+        "pa_bm_deallocate": [P, L], "pa_bm_seq_info": [P, L, IP, IP, IP],
+        "pa_bm_block_table": [P, L, P, I], "pa_bm_free_list": [P, P, I],
+        "pa_bm_ref_count": [P, I], "pa_bm_prepare_decode": [P, P, I, I, P, P, P],
+        "pa_bm_prepare_prefill": [P, P, I, I, P, P, P, P, I, IP, IP],
+    }
+    for name, args in bm_sigs.items():
+        getattr(lib, name).argtypes = args
+        getattr(lib, name).restype = I
     _lib = lib
     return lib
 
@@ -463,6 +490,119 @@ class DecodeGraph:
     def close(self) -> None:
         if getattr(self, "_h", None) is not None and self._h.value:
             self._lib.pa_decode_graph_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class BlockManager:
+    """Host block manager with prefix caching (the library's C++ implementation).
+
+    Sequences are named by integer ids.  Methods raise :class:`PagedAttnError` on errors
+    (``status`` PA_ERR_OUT_OF_BLOCKS = -6, PA_ERR_SEQUENCE = -7, ...); nothing touches the GPU.
+    """
+
+    def __init__(self, num_blocks: int, block_size: int, hash_bits: int = 64):
+        self._lib = load_library()
+        h = ctypes.c_void_p()
+        _raise_on("pa_bm_create", self._lib.pa_bm_create(int(num_blocks), int(block_size),
+                                                         int(hash_bits), ctypes.byref(h)))
+        self._h = h
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+
+    def _status(self, name, rc):
+        if rc < 0:
+            _raise_on(name, rc)
+        return rc
+
+    @property
+    def num_free(self) -> int:
+        return self._status("pa_bm_num_free", self._lib.pa_bm_num_free(self._h))
+
+    def can_allocate(self, num_tokens: int) -> bool:
+        return bool(self._status("pa_bm_can_allocate",
+                                 self._lib.pa_bm_can_allocate(self._h, int(num_tokens))))
+
+    def allocate(self, seq_id: int, tokens) -> int:
+        import numpy as np
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        cached = ctypes.c_int(0)
+        self._status("pa_bm_allocate", self._lib.pa_bm_allocate(
+            self._h, int(seq_id), t.ctypes.data_as(ctypes.c_void_p), int(t.size),
+            ctypes.byref(cached)))
+        return cached.value
+
+    def can_append(self, seq_id: int) -> bool:
+        return bool(self._status("pa_bm_can_append", self._lib.pa_bm_can_append(self._h, int(seq_id))))
+
+    def append(self, seq_id: int, token: int) -> None:
+        self._status("pa_bm_append", self._lib.pa_bm_append(self._h, int(seq_id), int(token)))
+
+    def deallocate(self, seq_id: int) -> None:
+        self._status("pa_bm_deallocate", self._lib.pa_bm_deallocate(self._h, int(seq_id)))
+
+    def seq_info(self, seq_id: int):
+        """(num_tokens, num_cached_tokens, num_blocks) of a live sequence."""
+        a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+        self._status("pa_bm_seq_info", self._lib.pa_bm_seq_info(
+            self._h, int(seq_id), ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+        return a.value, b.value, c.value
+
+    def block_table(self, seq_id: int):
+        import numpy as np
+        n = self._status("pa_bm_block_table", self._lib.pa_bm_block_table(self._h, int(seq_id), None, 0))
+        out = np.empty(n, dtype=np.int32)
+        self._lib.pa_bm_block_table(self._h, int(seq_id), out.ctypes.data_as(ctypes.c_void_p), n)
+        return out.tolist()
+
+    def free_list(self):
+        import numpy as np
+        n = self._status("pa_bm_free_list", self._lib.pa_bm_free_list(self._h, None, 0))
+        out = np.empty(n, dtype=np.int32)
+        self._lib.pa_bm_free_list(self._h, out.ctypes.data_as(ctypes.c_void_p), n)
+        return out.tolist()
+
+    def ref_count(self, block_id: int) -> int:
+        return self._status("pa_bm_ref_count", self._lib.pa_bm_ref_count(self._h, int(block_id)))
+
+    def prepare_decode(self, seq_ids, max_blocks_per_seq: int):
+        """(slot_mapping [B], context_lens [B], block_tables [B, MBS]) int32 arrays."""
+        import numpy as np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        B = int(ids.size)
+        slots = np.empty(B, np.int32)
+        lens = np.empty(B, np.int32)
+        tables = np.empty((B, int(max_blocks_per_seq)), np.int32)
+        vp = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+        self._status("pa_bm_prepare_decode", self._lib.pa_bm_prepare_decode(
+            self._h, vp(ids), B, int(max_blocks_per_seq), vp(slots), vp(lens), vp(tables)))
+        return slots, lens, tables
+
+    def prepare_prefill(self, seq_ids, max_blocks_per_seq: int):
+        """dict of cu_seqlens_q, context_lens, block_tables, slot_mapping, total_q, max_q_len."""
+        import numpy as np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        B = int(ids.size)
+        cap = sum(self.seq_info(i)[0] - self.seq_info(i)[1] for i in ids.tolist())
+        cu = np.empty(B + 1, np.int32)
+        lens = np.empty(B, np.int32)
+        tables = np.empty((B, int(max_blocks_per_seq)), np.int32)
+        slots = np.empty(max(cap, 1), np.int32)
+        tq, mq = ctypes.c_int(), ctypes.c_int()
+        vp = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+        self._status("pa_bm_prepare_prefill", self._lib.pa_bm_prepare_prefill(
+            self._h, vp(ids), B, int(max_blocks_per_seq), vp(cu), vp(lens), vp(tables), vp(slots),
+            int(cap), ctypes.byref(tq), ctypes.byref(mq)))
+        return {"cu_seqlens_q": cu, "context_lens": lens, "block_tables": tables,
+                "slot_mapping": slots[:tq.value], "total_q": tq.value, "max_q_len": mq.value}
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._lib.pa_bm_destroy(self._h)
             self._h = None
 
     def __del__(self):

@@ -13,9 +13,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpagedattn.so")
-SOURCES = ["pagedattn.hip", "store_gather.hip", "decode.hip", "prefill.hip", "graph.hip"]
+SOURCES = ["pagedattn.hip", "store_gather.hip", "decode.hip", "prefill.hip", "graph.hip",
+           "block_manager.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CXX = os.environ.get("CXX", "g++")
 ARCH = "gfx950"
 # Packed fp32 VALU ops are switched off for the device code (the host pass
 # prints a harmless "not a recognized feature" warning for it).
@@ -35,10 +37,13 @@ def _run(cmd):
 def build(verbose: bool = False) -> str:
     """Compile every source and link ``libpagedattn.so``; returns its path."""
     os.makedirs(OBJDIR, exist_ok=True)
-    objs = [os.path.join(OBJDIR, s.replace(".hip", ".o")) for s in SOURCES]
+    objs = [os.path.join(OBJDIR, os.path.splitext(s)[0] + ".o") for s in SOURCES]
 
     def compile_one(src_obj):
         src, obj = src_obj
+        if src.endswith(".cpp"):  # host-only C++
+            return _run([CXX, "-O2", "-std=c++17", "-fPIC", "-Wall", "-c", os.path.join(CSRC, src),
+                         "-o", obj])
         return _run([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
 
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:

@@ -42,7 +42,9 @@ const char* pa_status_string(int status) {
     case PA_ERR_SHAPE: return "PA_ERR_SHAPE: invalid or inconsistent size";
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: head_dim, block_size or dtype not supported";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: decode workspace missing or too small";
-    case PA_ERR_HIP: return "PA_ERR_HIP: kernel launch failed";
+    case PA_ERR_HIP: return "PA_ERR_HIP: kernel launch or HIP call failed";
+    case PA_ERR_OUT_OF_BLOCKS: return "PA_ERR_OUT_OF_BLOCKS: not enough free KV blocks";
+    case PA_ERR_SEQUENCE: return "PA_ERR_SEQUENCE: unknown or already allocated sequence";
     default: return "unknown pa_status";
   }
 }

@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--copy-probe", action="store_true",
@@ -390,6 +391,42 @@ def main():
                 "new_tokens_per_s": round(p.total_q / (pstep * 1e-3), 1)}
         except Exception as e:  # prefill not available: report, do not hide the decode result
             result["prefill"] = {"error": str(e)}
+
+    # ---------------------------------------------------------------- mixed step (extra leg)
+    if not args.no_mixed:
+        from workloads import mixed_case
+        r = np.random.default_rng(8606)
+        mP = r.integers(0, 3584, size=16, endpoint=True)
+        mD = r.integers(128, 4096, size=64, endpoint=True)
+        m = mixed_case(8606, mP, [512] * 16, mD, 16, 8, 128, 256, max_blocks_per_seq=16)
+        mk, mv = bf16(m.k_cache), bf16(m.v_cache)
+        mq, mkn, mvn = bf16(m.q), bf16(m.k_new), bf16(m.v_new)
+        mslots, mcu, mbt, mctx = (i32(m.slot_mapping), i32(m.cu_seqlens_q[:17]),
+                                  i32(m.block_tables), i32(m.context_lens))
+        mout = torch.empty((m.total_q, 16, 128), dtype=torch.bfloat16, device=dev)
+        mws = pa.decode_workspace(pa.decode_workspace_bytes(64, 16, 8, 128, 256, 16), dev)
+        side = torch.cuda.Stream(device=dev)
+        ptok = int(m.cu_seqlens_q[16])
+
+        def mixed(ds=None):
+            pa.paged_attention_mixed(mq, mkn, mvn, mslots, mcu, mbt, mctx, mout, k_cache=mk,
+                                     v_cache=mv, num_prefill_seqs=16, prefill_tokens=ptok,
+                                     max_prefill_q_len=512, scale=m.scale, workspace=mws,
+                                     decode_stream=ds)
+
+        ms_seq, _, _, _ = timed_loop(torch, nothing, mixed, max(10, args.steps // 2),
+                                     max(3, args.warmup // 2), flush)
+        ms_con, _, _, _ = timed_loop(torch, nothing, lambda: mixed(side), max(10, args.steps // 2),
+                                     max(3, args.warmup // 2), flush)
+        pairs = 0
+        for p_, n_ in zip(m.prefix_lens, m.q_lens):
+            pairs += int(n_) * int(p_) + int(n_) * (int(n_) + 1) // 2
+        result["mixed_step"] = {
+            "workload": "one call: 16 chunks x 512 new tokens (prefix U[0,3584]) + 64 decode rows "
+                        "(ctx U[128,4096]), 16 q / 8 kv heads, head_dim 128, block 256, one pool",
+            "ms_one_stream": round(ms_seq, 5), "ms_decode_on_second_stream": round(ms_con, 5),
+            "tokens_per_s": round(m.total_q / (min(ms_seq, ms_con) * 1e-3), 1),
+            "flops": 4 * 16 * 128 * pairs}
 
     # ---------------------------------------------------------------- CPU oracle
     if not args.no_cpu_baseline:

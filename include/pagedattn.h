@@ -272,6 +272,40 @@ int pa_paged_prefill(const void* q, const void* k_new, const void* v_new,
                      void* out, int out_dtype, void* stream);
 
 /*
+ * Mixed prefill + decode step in one call: chunks and single decode tokens
+ * under one cu_seqlens_q ("Nano-vLLM源码学习(2)" §2: prefill and decode both
+ * read paged KV through block_table; the VLLM 0.7.3 source article §3.2: one
+ * iteration batches new requests' prefill with running requests' decode).
+ * Sequences 0 .. num_prefill_seqs-1 are chunks over rows 0 .. prefill_tokens-1
+ * (cu_seqlens_q [num_prefill_seqs+1], device, as for pa_paged_prefill; any
+ * q_len >= 0); sequences num_prefill_seqs .. +num_decode_seqs-1 have one row
+ * each, rows prefill_tokens + i (a decode row is a chunk of one token).
+ *   q [prefill_tokens + num_decode_seqs, Hq, D]; k_new, v_new and
+ *   slot_mapping [prefill_tokens + num_decode_seqs] rows: every new token's
+ *   K/V and slot; block_tables [num_prefill_seqs + num_decode_seqs, MBS] and
+ *   context_lens (prefix + q_len) in the same sequence order; out like q.
+ *   workspace: pa_paged_decode_workspace_bytes(num_decode_seqs, ...).
+ * Effect: every new token is stored (slot < 0 skips), then each row attends
+ * to its sequence's keys 0 .. its position, as pa_paged_prefill would for a
+ * q_len-1 chunk and as pa_paged_decode does.  The chunks' tokens are stored
+ * before any chunk is attended, so a chunk may read a block another chunk of
+ * the same call fills.  The decode rows run as pa_paged_decode_append; with
+ * decode_stream != NULL and != stream they run on decode_stream, forked from
+ * and joined back into `stream` with events (the call then returns with all
+ * of its work ordered before later work on `stream`).  decode_stream must
+ * have default priority.
+ */
+int pa_paged_attention_mixed(const void* q, const void* k_new, const void* v_new,
+                             const int32_t* slot_mapping, const int32_t* cu_seqlens_q,
+                             int num_prefill_seqs, int num_decode_seqs, int prefill_tokens,
+                             int max_prefill_q_len, void* k_cache, void* v_cache,
+                             const int32_t* block_tables, int max_blocks_per_seq,
+                             const int32_t* context_lens, int num_q_heads, int num_kv_heads,
+                             int head_dim, int block_size, int num_blocks, float scale, void* out,
+                             int out_dtype, void* workspace, size_t workspace_bytes, void* stream,
+                             void* decode_stream);
+
+/*
  * Test aid: un-page one cache (MinivLLM guide §4.5 block_tables).
  *   cache         [num_blocks, block_size, num_kv_heads, head_dim] bf16
  *   cu_seqlens_k  [B+1] int32 (device): prefix sums of context_lens

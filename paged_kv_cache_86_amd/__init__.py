@@ -40,6 +40,7 @@ EXPORTED_SYMBOLS = (
     "pa_decode_graph_bucket",
     "pa_decode_graph_run",
     "pa_decode_graph_destroy",
+    "pa_paged_attention_mixed",
     "pa_bm_create",
     "pa_bm_destroy",
     "pa_bm_num_free",
@@ -112,6 +113,9 @@ def load_library() -> ctypes.CDLL:
     lib.pa_decode_graph_run.restype = I
     lib.pa_decode_graph_destroy.argtypes = [P]
     lib.pa_decode_graph_destroy.restype = I
+    lib.pa_paged_attention_mixed.argtypes = [P, P, P, P, P, I, I, I, I, P, P, P, I, P, I, I, I, I,
+                                             I, F, P, I, P, Z, P, P]
+    lib.pa_paged_attention_mixed.restype = I
     L, IP = ctypes.c_int64, ctypes.POINTER(ctypes.c_int)
     bm_sigs = {
         "pa_bm_create": [I, I, I, PP], "pa_bm_destroy": [P], "pa_bm_num_free": [P],
@@ -359,6 +363,49 @@ def paged_prefill(q, k_new, v_new, cu_seqlens_q, block_tables, context_lens, out
         _ptr(v_cache), _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), Hq, Hkv,
         D, BS, NB, sc, _ptr(out), _out_dtype(out), _stream(q.device))
     _raise_on("pa_paged_prefill", rc)
+
+
+def paged_attention_mixed(q, k_new, v_new, slot_mapping, cu_seqlens_q, block_tables,
+                          context_lens, out, *, k_cache, v_cache, num_prefill_seqs: int,
+                          prefill_tokens: int, max_prefill_q_len: Optional[int] = None,
+                          scale: Optional[float] = None, workspace=None,
+                          decode_stream=None) -> None:
+    """Store every new token, then attend: chunks (sequences 0..num_prefill_seqs-1, rows
+    0..prefill_tokens-1) and one-token decode rows (the remaining sequences, one row each)."""
+    torch = _torch()
+    NB, BS, Hkv, D = _cache_geometry(k_cache, v_cache)
+    _check(q, torch.bfloat16, "q", 3)
+    _check(k_new, torch.bfloat16, "k_new", 3)
+    _check(v_new, torch.bfloat16, "v_new", 3)
+    _check(slot_mapping, torch.int32, "slot_mapping", 1)
+    _check(cu_seqlens_q, torch.int32, "cu_seqlens_q", 1)
+    _check(block_tables, torch.int32, "block_tables", 2)
+    _check(context_lens, torch.int32, "context_lens", 1)
+    T, Hq, Dq = (int(x) for x in q.shape)
+    B = int(context_lens.shape[0])
+    P = int(num_prefill_seqs)
+    nd = B - P
+    if Dq != D or tuple(k_new.shape) != (T, Hkv, D) or tuple(v_new.shape) != (T, Hkv, D):
+        raise ValueError("q / k_new / v_new shapes disagree with the cache")
+    if T != int(prefill_tokens) + nd or slot_mapping.shape[0] != T:
+        raise ValueError("rows must be prefill_tokens + one per decode sequence")
+    if block_tables.shape[0] != B or cu_seqlens_q.shape[0] < P + 1:
+        raise ValueError("block_tables [B, MBS] and cu_seqlens_q [>= num_prefill_seqs+1] expected")
+    _check(out, out.dtype, "out", 3)
+    if tuple(out.shape) != (T, Hq, D):
+        raise ValueError(f"out must be [{T}, {Hq}, {D}]")
+    MBS = int(block_tables.shape[1])
+    need = decode_workspace_bytes(nd, Hq, Hkv, D, BS, MBS) if nd > 0 else 0
+    workspace = _workspace_for(workspace, need, q.device)
+    sc = float(scale) if scale is not None else 0.0
+    mq = int(prefill_tokens) if max_prefill_q_len is None else int(max_prefill_q_len)
+    ds = ctypes.c_void_p(decode_stream.cuda_stream) if decode_stream is not None else None
+    rc = load_library().pa_paged_attention_mixed(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(cu_seqlens_q), P, nd,
+        int(prefill_tokens), mq, _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), MBS,
+        _ptr(context_lens), Hq, Hkv, D, BS, NB, sc, _ptr(out), _out_dtype(out), _ptr(workspace),
+        int(workspace.numel()), _stream(q.device), ds)
+    _raise_on("pa_paged_attention_mixed", rc)
 
 
 def paged_gather(cache, block_tables, context_lens, cu_seqlens_k, max_context_len: int, out) -> None:

@@ -289,6 +289,84 @@ int pa_paged_prefill(const void* q, const void* k_new, const void* v_new,
   return rc == 0 ? PA_OK : PA_ERR_HIP;
 }
 
+int pa_paged_attention_mixed(const void* q, const void* k_new, const void* v_new,
+                             const int32_t* slot_mapping, const int32_t* cu_seqlens_q,
+                             int num_prefill_seqs, int num_decode_seqs, int prefill_tokens,
+                             int max_prefill_q_len, void* k_cache, void* v_cache,
+                             const int32_t* block_tables, int max_blocks_per_seq,
+                             const int32_t* context_lens, int num_q_heads, int num_kv_heads,
+                             int head_dim, int block_size, int num_blocks, float scale, void* out,
+                             int out_dtype, void* workspace, size_t workspace_bytes, void* stream,
+                             void* decode_stream) {
+  if (num_prefill_seqs < 0 || num_decode_seqs < 0 || prefill_tokens < 0 || max_prefill_q_len < 0)
+    return PA_ERR_SHAPE;
+  if (num_prefill_seqs == 0 && prefill_tokens != 0) return PA_ERR_SHAPE;
+  if (max_prefill_q_len > prefill_tokens) return PA_ERR_SHAPE;
+  if (num_prefill_seqs + num_decode_seqs == 0) return PA_OK;
+  int bs_log2 = 0;
+  const int g = check_geometry(num_kv_heads, head_dim, block_size, num_blocks, &bs_log2);
+  if (g != PA_OK) return g;
+  if (num_q_heads <= 0 || num_q_heads % num_kv_heads != 0 || max_blocks_per_seq <= 0)
+    return PA_ERR_SHAPE;
+  if (out_dtype != PA_BF16 && out_dtype != PA_F32) return PA_ERR_UNSUPPORTED;
+  if (!q || !k_new || !v_new || !slot_mapping || !k_cache || !v_cache || !block_tables ||
+      !context_lens || !out || (num_prefill_seqs > 0 && !cu_seqlens_q))
+    return PA_ERR_NULL;
+  if (num_decode_seqs > 0) {
+    const size_t need = pa_paged_decode_workspace_bytes(num_decode_seqs, num_q_heads, num_kv_heads,
+                                                        head_dim, block_size, max_blocks_per_seq);
+    if (need == 0) return PA_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+  }
+  // 1. the chunks' new K/V go into the cache first: a sequence of this step may
+  //    reuse a block another one fills in this step, and reads it from the cache
+  int rc = pa_kvcache_store(k_new, v_new, slot_mapping, prefill_tokens, k_cache, v_cache,
+                            num_blocks, block_size, num_kv_heads, head_dim, stream);
+  if (rc != PA_OK) return rc;
+  // 2. the decode rows, optionally on a second stream that joins back afterwards
+  hipStream_t s = (hipStream_t)stream;
+  hipStream_t ds = decode_stream ? (hipStream_t)decode_stream : s;
+  hipEvent_t fork = nullptr, join = nullptr;
+  if (num_decode_seqs > 0 && ds != s) {
+    if (hipEventCreateWithFlags(&fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&join, hipEventDisableTiming) != hipSuccess ||
+        hipEventRecord(fork, s) != hipSuccess || hipStreamWaitEvent(ds, fork, 0) != hipSuccess) {
+      if (fork) (void)hipEventDestroy(fork);
+      if (join) (void)hipEventDestroy(join);
+      return PA_ERR_HIP;
+    }
+  }
+  if (num_decode_seqs > 0) {
+    const size_t qrow = (size_t)num_q_heads * head_dim;
+    const size_t kvrow = (size_t)num_kv_heads * head_dim;
+    const size_t orow = qrow * (out_dtype == PA_F32 ? 4 : 2);
+    rc = pa_paged_decode_append(
+        (const uint16_t*)q + (size_t)prefill_tokens * qrow,
+        (const uint16_t*)k_new + (size_t)prefill_tokens * kvrow,
+        (const uint16_t*)v_new + (size_t)prefill_tokens * kvrow, slot_mapping + prefill_tokens,
+        k_cache, v_cache, block_tables + (size_t)num_prefill_seqs * max_blocks_per_seq,
+        max_blocks_per_seq, context_lens + num_prefill_seqs, num_decode_seqs, num_q_heads,
+        num_kv_heads, head_dim, block_size, num_blocks, scale,
+        (char*)out + (size_t)prefill_tokens * orow, out_dtype, workspace, workspace_bytes, ds);
+  }
+  // 3. the chunks
+  if (rc == PA_OK && num_prefill_seqs > 0 && prefill_tokens > 0)
+    rc = pa_paged_prefill(q, k_new, v_new, cu_seqlens_q, num_prefill_seqs, prefill_tokens,
+                          max_prefill_q_len > 0 ? max_prefill_q_len : prefill_tokens, k_cache,
+                          v_cache, block_tables, max_blocks_per_seq, context_lens, num_q_heads,
+                          num_kv_heads, head_dim, block_size, num_blocks, scale, out, out_dtype,
+                          stream);
+  if (fork) {
+    // join even after an error, so the caller's stream never runs ahead of the decode work
+    const bool ok = hipEventRecord(join, ds) == hipSuccess &&
+                    hipStreamWaitEvent(s, join, 0) == hipSuccess;
+    (void)hipEventDestroy(fork);
+    (void)hipEventDestroy(join);
+    if (!ok && rc == PA_OK) rc = PA_ERR_HIP;
+  }
+  return rc;
+}
+
 int pa_paged_gather(const void* cache, const int32_t* block_tables, int max_blocks_per_seq,
                     const int32_t* context_lens, const int32_t* cu_seqlens_k, int num_seqs,
                     int max_context_len, int num_kv_heads, int head_dim, int block_size,

@@ -14,6 +14,7 @@ from .synth import (  # noqa: F401
     config,
     cu_seqlens_from_lens,
     decode_case,
+    mixed_case,
     prefill_case,
     slot_for_position,
 )

@@ -377,6 +377,22 @@ def prefill_case(seed: int, prefix_lens, q_lens, num_q_heads: int, num_kv_heads:
                          k_new=k_new, v_new=v_new, slot_mapping=slots, logical_k=lk, logical_v=lv)
 
 
+def mixed_case(seed: int, chunk_prefix_lens, chunk_q_lens, decode_context_lens, num_q_heads: int,
+               num_kv_heads: int, head_dim: int, block_size: int, *,
+               num_blocks: Optional[int] = None, max_blocks_per_seq: Optional[int] = None,
+               name: str = "mixed") -> PrefillInputs:
+    """A batch of prefill chunks followed by one-token decode rows, in one pool.
+
+    A decode row of context ``c`` is a chunk of one token over a prefix of ``c - 1``; the
+    returned inputs list the chunks first, then the decode sequences.
+    """
+    dctx = np.asarray(decode_context_lens, dtype=np.int32)
+    P = np.concatenate([np.asarray(chunk_prefix_lens, np.int32), dctx - 1]).astype(np.int32)
+    n = np.concatenate([np.asarray(chunk_q_lens, np.int32), np.ones_like(dctx)]).astype(np.int32)
+    return prefill_case(seed, P, n, num_q_heads, num_kv_heads, head_dim, block_size,
+                        num_blocks=num_blocks, max_blocks_per_seq=max_blocks_per_seq, name=name)
+
+
 def _config4_sharing(rng, ctx, n_groups=13, group_size=4, block_size=256):
     eligible = np.nonzero(ctx > block_size)[0]
     chosen = rng.choice(eligible, size=n_groups * group_size, replace=False)

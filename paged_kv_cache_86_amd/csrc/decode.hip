@@ -44,10 +44,17 @@ constexpr int kMaxSplitBlocks = 512;  // split tokens / block size (block size >
 //
 // APPEND fuses the store of each sequence's new token: position ctx-1 is not
 // read from the cache but from k_new / v_new (quantized first for KV8, exactly
-// as the store kernel does), staged in LDS and folded into the softmax state
-// of the split that holds it; the workgroup of that split with sub-group 0
-// also writes the row into its cache slot.
-template <int D, int GT, int U, int NIT, bool PRELOAD, bool NT, bool KV8, bool APPEND>
+// as the store kernel does).  The first 2*D/8 lanes of wave 0 load the row at
+// the start; after the main loop the workgroup of the split that holds the
+// token passes it between lanes of wave 0 (no LDS, no barrier) and folds it
+// into row slot 0's softmax state, and the one of head sub-group 0 writes it
+// into its cache slot.
+//
+// ONE_BLOCK is set when one cache block covers a whole split (block_size >=
+// split length): the split's block id is then a single scalar load, with no
+// LDS staging and no barrier before the K/V loads.
+template <int D, int GT, int U, int NIT, bool PRELOAD, bool NT, bool KV8, bool APPEND,
+          bool ONE_BLOCK>
 __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
   constexpr int EB = KV8 ? 1 : 2;   // bytes per K/V element
   constexpr int EPL = 16 / EB;      // elements per lane per 16-byte load
@@ -57,12 +64,11 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
   constexpr int CH = U * RPW;    // tokens per wave chunk
   constexpr int S = kWaves * NIT * CH;  // tokens per split
 
-  __shared__ int s_blk[kMaxSplitBlocks];
+  __shared__ int s_blk[ONE_BLOCK ? 1 : kMaxSplitBlocks];
   __shared__ float s_m[kWaves][GT];
   __shared__ float s_l[kWaves][GT];
   __shared__ float s_acc[kWaves][GT][D];
   constexpr int NLB = D / 8;  // 16-byte bf16 vectors per new K (or V) row of one head
-  __shared__ u32x4 s_new[APPEND ? 2 : 1][APPEND ? NLB : 1];  // new K, V row (bf16 or codes)
 
   const int bid = blockIdx.x;
   const int hg = bid % a.hg;
@@ -84,14 +90,23 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
 
   // Issued before the context length is known, so the three loads overlap:
   // table entries of this split (clamped to the table row), q, context length.
-  const int nb_max = S > (1 << a.bs_log2) ? (S >> a.bs_log2) : 1;
+  // When one block covers the whole split, its id is a single (scalar) load
+  // and no LDS staging or barrier is needed before the K/V loads.
+  constexpr bool one_block = ONE_BLOCK;
+  int blk0 = -1;
+  if constexpr (one_block) {
+    const int blk = a.block_tables[(int64_t)seq * a.mbs + b0];  // b0 < mbs for every split
+    blk0 = (blk >= 0 && blk < a.num_blocks) ? blk : -1;
+  } else {
+    const int nb_max = S >> a.bs_log2;
 #pragma unroll
-  for (int k = 0; k < kMaxSplitBlocks / 256; ++k) {
-    const int i = tid + 256 * k;
-    if (i < nb_max) {
-      int blk = -1;
-      if (b0 + i < a.mbs) blk = a.block_tables[(int64_t)seq * a.mbs + b0 + i];
-      s_blk[i] = (blk >= 0 && blk < a.num_blocks) ? blk : -1;
+    for (int k = 0; k < kMaxSplitBlocks / 256; ++k) {
+      const int i = tid + 256 * k;
+      if (i < nb_max) {
+        int blk = -1;
+        if (b0 + i < a.mbs) blk = a.block_tables[(int64_t)seq * a.mbs + b0 + i];
+        s_blk[i] = (blk >= 0 && blk < a.num_blocks) ? blk : -1;
+      }
     }
   }
   // Heads past the group's end (last sub-group) re-read its last head; their
@@ -123,24 +138,27 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
   ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
   const int nsplit = ctx == 0 ? 1 : (ctx + S - 1) / S;
 
-  // APPEND: the workgroup of the last split stages the new row (as codes for
-  // KV8) in LDS; the one of sub-group 0 also stores it into the cache.
-  if constexpr (APPEND) {
-    if (new_lane && split == nsplit - 1) {
-      const int64_t dst = ((int64_t)slot * a.Hkv + kvh) * D + new_c * 8;  // element index
-      const bool store = sub == 0 && slot >= 0 && (int64_t)slot < a.num_slots;
-      if constexpr (KV8) {
-        const u32x2 cw = quantize8(xnew, new_is_v ? a.qscale_v : a.qscale_k);
-        ((u32x2*)&s_new[new_is_v][0])[new_c] = cw;
-        if (store) *(u32x2*)((char*)(new_is_v ? a.v_cache_w : a.k_cache_w) + dst) = cw;
-      } else {
-        s_new[new_is_v][new_c] = xnew;
-        if (store) *(u32x4*)((uint16_t*)(new_is_v ? a.v_cache_w : a.k_cache_w) + dst) = xnew;
-      }
+  // APPEND: lanes 0 .. 2*NLB-1 of wave 0 write the new row (bf16, or E4M3
+  // codes for KV8) into its slot when this is the sequence's last split and
+  // head sub-group 0; every lane returns its vector (codes in .x, .y for KV8).
+  auto store_new = [&]() -> u32x4 {
+    u32x4 v = xnew;
+    if constexpr (KV8) {
+      const u32x2 cw = quantize8(xnew, new_is_v ? a.qscale_v : a.qscale_k);
+      v = u32x4{cw.x, cw.y, 0u, 0u};
     }
-  }
+    if (new_lane && sub == 0 && slot >= 0 && (int64_t)slot < a.num_slots) {
+      const int64_t dst = ((int64_t)slot * a.Hkv + kvh) * D + new_c * 8;  // element index
+      if constexpr (KV8) *(u32x2*)((char*)(new_is_v ? a.v_cache_w : a.k_cache_w) + dst) = u32x2{v.x, v.y};
+      else *(u32x4*)((uint16_t*)(new_is_v ? a.v_cache_w : a.k_cache_w) + dst) = v;
+    }
+    return v;
+  };
 
   if (ctx == 0) {  // padded row: output zeros
+    if constexpr (APPEND) {
+      if (split == 0 && w == 0) (void)store_new();
+    }
     if (split == 0) {
       for (int i = tid; i < gh * D; i += blockDim.x) {
         const int64_t o = ((int64_t)seq * a.Hq + h0) * D + i;
@@ -157,7 +175,7 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
   const int tc = APPEND ? ctx - 1 : ctx;
   const int t1 = min(tc, t0 + S);
   const int jfill = t1 > t0 ? t1 - 1 : t0;
-  __syncthreads();
+  if constexpr (!one_block) __syncthreads();  // s_blk written
 
   const int64_t row_stride = (int64_t)a.Hkv * D;
   const int64_t head_off = (int64_t)kvh * D + c * EPL;  // elements
@@ -218,7 +236,9 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
       // are masked out of the softmax below.
       const int j = t0 + (it * kWaves + w) * CH + u * RPW + r;
       const int jj = j < t1 ? j : jfill;
-      int blk = s_blk[(jj >> a.bs_log2) - b0];
+      int blk;
+      if constexpr (one_block) blk = blk0;
+      else blk = s_blk[(jj >> a.bs_log2) - b0];
       ok[u] = (j < t1) && (blk >= 0);
       blk = blk < 0 ? 0 : blk;
       const int64_t off = (((int64_t)blk << a.bs_log2) + (jj & bs_mask)) * row_stride + head_off;
@@ -311,8 +331,21 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
   // APPEND: row slot 0 of wave 0 takes the new token (last split only).
   if constexpr (APPEND) {
     if (split == nsplit - 1 && w == 0) {
-      const u32x4 kx = s_new[0][c];
-      const u32x4 vx = s_new[1][c];
+      const u32x4 nv = store_new();
+      // lane c's part of the row: vector c (bf16) or the codes of vectors 2c, 2c+1 (KV8)
+      u32x4 kx, vx;
+      if constexpr (KV8) {
+        const int sk = 2 * c, sv = NLB + 2 * c;
+        kx = u32x4{(uint32_t)__shfl((int)nv.x, sk), (uint32_t)__shfl((int)nv.y, sk),
+                   (uint32_t)__shfl((int)nv.x, sk + 1), (uint32_t)__shfl((int)nv.y, sk + 1)};
+        vx = u32x4{(uint32_t)__shfl((int)nv.x, sv), (uint32_t)__shfl((int)nv.y, sv),
+                   (uint32_t)__shfl((int)nv.x, sv + 1), (uint32_t)__shfl((int)nv.y, sv + 1)};
+      } else {
+        kx = u32x4{(uint32_t)__shfl((int)nv.x, c), (uint32_t)__shfl((int)nv.y, c),
+                   (uint32_t)__shfl((int)nv.z, c), (uint32_t)__shfl((int)nv.w, c)};
+        vx = u32x4{(uint32_t)__shfl((int)nv.x, NLB + c), (uint32_t)__shfl((int)nv.y, NLB + c),
+                   (uint32_t)__shfl((int)nv.z, NLB + c), (uint32_t)__shfl((int)nv.w, NLB + c)};
+      }
       float sn[GT];
 #pragma unroll
       for (int h = 0; h < GT; ++h) sn[h] = mul_rn(group_sum<LPR>(kdot(h, kx)), a.scale_log2e);
@@ -410,7 +443,6 @@ template <int D, int GT, int S>
 __global__ __launch_bounds__(256) void paged_decode_combine_kernel(DecodeArgs a) {
   constexpr int ITEMS = (GT * D + 255) / 256;  // (head, dim) outputs per thread
   __shared__ float s_w[kDecodeMaxSplits][GT];  // per split: 2^(m_s - M) / L
-  __shared__ float s_ml[kDecodeMaxSplits][GT][2];
   const int unit = blockIdx.x;
   const int hg = unit % a.hg;
   const int seq = unit / a.hg;
@@ -429,9 +461,26 @@ __global__ __launch_bounds__(256) void paged_decode_combine_kernel(DecodeArgs a)
       pre[k][sp] = a.ws_o[(p0 + (int64_t)spc * GT + h) * D + d];
     }
   }
-  for (int i = tid; i < a.nsplit_max * GT; i += blockDim.x) {
-    s_ml[i / GT][i % GT][0] = a.ws_ml[2 * (p0 + i)];
-    s_ml[i / GT][i % GT][1] = a.ws_ml[2 * (p0 + i) + 1];
+  // (m, l) of every split: wave w reduces heads w, w + 4, ...; lane i holds
+  // splits i, i + 64, ...  (loaded before the context length is known).
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  constexpr int HPW = (GT + kWaves - 1) / kWaves;           // heads per wave
+  constexpr int SPL = (kDecodeMaxSplits + 63) / 64;         // splits per lane
+  float mv[HPW][SPL], lv[HPW][SPL];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const int h = min(w + kWaves * hh, GT - 1);
+#pragma unroll
+    for (int k = 0; k < SPL; ++k) {
+      const int sp = lane + 64 * k;
+      mv[hh][k] = kNegBig;
+      lv[hh][k] = 0.f;
+      if (sp < a.nsplit_max) {
+        mv[hh][k] = a.ws_ml[2 * (p0 + (int64_t)sp * GT + h)];
+        lv[hh][k] = a.ws_ml[2 * (p0 + (int64_t)sp * GT + h) + 1];
+      }
+    }
   }
   int ctx = a.context_lens[seq];
   const int cap = a.mbs << a.bs_log2;
@@ -442,15 +491,28 @@ __global__ __launch_bounds__(256) void paged_decode_combine_kernel(DecodeArgs a)
   const int sub = hg - kvh * a.nsub;
   const int h0 = kvh * a.group + sub * GT;
   const int gh = min(GT, a.group - sub * GT);
-  __syncthreads();
-  if (tid < GT) {
-    const int h = tid;
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const int h = w + kWaves * hh;
+    if (h >= GT) break;  // wave-uniform
     float M = kNegBig;
-    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, s_ml[sp][h][0]);
+#pragma unroll
+    for (int k = 0; k < SPL; ++k)
+      if (lane + 64 * k < nsplit) M = fmaxf(M, mv[hh][k]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, shfl_xor(M, off));
     float L = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) L += s_ml[sp][h][1] * __builtin_amdgcn_exp2f(s_ml[sp][h][0] - M);
+#pragma unroll
+    for (int k = 0; k < SPL; ++k)
+      if (lane + 64 * k < nsplit) L += lv[hh][k] * __builtin_amdgcn_exp2f(mv[hh][k] - M);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) L += shfl_xor(L, off);
     const float inv = L > 0.f ? 1.f / L : 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) s_w[sp][h] = __builtin_amdgcn_exp2f(s_ml[sp][h][0] - M) * inv;
+#pragma unroll
+    for (int k = 0; k < SPL; ++k) {
+      const int sp = lane + 64 * k;
+      if (sp < nsplit) s_w[sp][h] = __builtin_amdgcn_exp2f(mv[hh][k] - M) * inv;
+    }
   }
   __syncthreads();
 #pragma unroll
@@ -491,9 +553,14 @@ constexpr int split_tokens() {
 template <int D, int GT, bool KV8, bool APPEND>
 int launch_d(const DecodeArgs& a, int B, hipStream_t stream) {
   const int64_t nwg = (int64_t)B * a.hg * a.nsplit_max;
-  hipLaunchKernelGGL((paged_decode_kernel<D, GT, tile_u<KV8>(), tile_nit<KV8>(), kPreload,
-                                          kNontemporal, KV8, APPEND>),
-                     dim3((unsigned)nwg), dim3(256), 0, stream, a);
+  if ((1 << a.bs_log2) >= split_tokens<D, KV8>())
+    hipLaunchKernelGGL((paged_decode_kernel<D, GT, tile_u<KV8>(), tile_nit<KV8>(), kPreload,
+                                            kNontemporal, KV8, APPEND, true>),
+                       dim3((unsigned)nwg), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((paged_decode_kernel<D, GT, tile_u<KV8>(), tile_nit<KV8>(), kPreload,
+                                            kNontemporal, KV8, APPEND, false>),
+                       dim3((unsigned)nwg), dim3(256), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return -1;
   if (a.nsplit_max > 1) {
     hipLaunchKernelGGL((paged_decode_combine_kernel<D, GT, split_tokens<D, KV8>()>),

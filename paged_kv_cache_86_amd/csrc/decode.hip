@@ -17,11 +17,16 @@
 //     LDS across waves);
 //   * split-K partials (m, l, unnormalised o) go to the workspace and a
 //     second, small kernel merges them in split order (deterministic); a
-//     context that fits in one split writes its output directly.  The
+//     context that fits in one split writes its output directly;
+//   * splits come in two lengths when the grid is large enough: a context
+//     that would need more short splits than the grid has slots per sequence
+//     takes splits of twice the length instead.  The
 //     kernel boundary is what makes one XCD's partials visible to another:
 //     an in-kernel "last workgroup merges" scheme needs a device-scope
 //     release/acquire per workgroup, which on this chip writes back and
 //     invalidates the whole L2 of an XCD and costs far more than a launch.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -30,12 +35,21 @@ namespace pa {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kMaxSplitBlocks = 512;  // split tokens / block size (block size >= 1)
+constexpr int kMaxSplitBlocks = 512;  // short-split tokens / block size (block size >= 1)
 
-// One workgroup = one (sequence, head group, split).  A split is
-// kWaves * NIT chunks of U * RPW tokens; wave w takes chunks w, w + 4, ...
-// The chunk loop is fully unrolled so that every K/V load of the wave can be
-// issued before the first one is consumed.
+
+// One workgroup = one (sequence, head group, split).
+//
+// Splits.  A short split is S = kWaves * NIT chunks of U * RPW tokens (wave w
+// takes chunks w, w + 4, ...).  With LONG, a context needing more than
+// nsplit_max short splits is cut into long splits of 2S tokens instead, so
+// one grid of nsplit_max workgroups per (sequence, head group) serves every
+// context the table allows: short contexts leave fewer workgroups idle, long
+// ones run fewer, longer workgroups (their per-workgroup set-up and merge are
+// paid half as often).  The chunk loop is fully unrolled: a short split issues
+// every load of the wave before the first is consumed (DEPTH == NIT); a long
+// split keeps DEPTH chunks in flight, issuing chunk it + DEPTH as it consumes
+// chunk it.
 //
 // KV8 selects an FP8 (OCP E4M3) cache: a 16-byte load then carries 16 codes
 // instead of 8 bf16 values.  K codes are widened to bf16 pairs and take the
@@ -50,21 +64,25 @@ constexpr int kMaxSplitBlocks = 512;  // split tokens / block size (block size >
 // into row slot 0's softmax state, and the one of head sub-group 0 writes it
 // into its cache slot.
 //
-// ONE_BLOCK is set when one cache block covers a whole split (block_size >=
-// split length): the split's block id is then a single scalar load, with no
-// LDS staging and no barrier before the K/V loads.
-template <int D, int GT, int U, int NIT, bool PRELOAD, bool NT, bool KV8, bool APPEND,
-          bool ONE_BLOCK>
-__global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
+// SCALAR_BLK is set when a cache block holds at least one short split
+// (block_size >= S): the split's block ids (one for a short split, two for a
+// long one) are then scalar loads, with no LDS staging and no barrier before
+// the K/V loads.  Otherwise the ids of the split are staged in LDS while the
+// context length is still in flight (long splits need SCALAR_BLK).
+template <int D, int GT, int U, int NIT, int DEPTH, int DEPTH_LONG, bool LONG, bool NT, bool KV8,
+          bool APPEND, bool SCALAR_BLK>
+__device__ __forceinline__ void paged_decode_body(const DecodeArgs& a) {
   constexpr int EB = KV8 ? 1 : 2;   // bytes per K/V element
   constexpr int EPL = 16 / EB;      // elements per lane per 16-byte load
   constexpr int LPR = D / EPL;      // lanes per K/V row of one head
   constexpr int RPW = 64 / LPR;     // rows per 64-lane load
   constexpr int QW = EPL / 8;       // 16-byte chunks of q per lane and head
-  constexpr int CH = U * RPW;    // tokens per wave chunk
-  constexpr int S = kWaves * NIT * CH;  // tokens per split
+  constexpr int CH = U * RPW;       // tokens per wave chunk
+  constexpr int S = kWaves * NIT * CH;  // tokens per short split
+  constexpr int SL = LONG ? 2 * S : S;  // tokens per long split
+  static_assert(!LONG || SCALAR_BLK, "long splits read scalar block ids");
 
-  __shared__ int s_blk[ONE_BLOCK ? 1 : kMaxSplitBlocks];
+  __shared__ int s_blk[SCALAR_BLK ? 1 : kMaxSplitBlocks];
   __shared__ float s_m[kWaves][GT];
   __shared__ float s_l[kWaves][GT];
   __shared__ float s_acc[kWaves][GT][D];
@@ -85,28 +103,31 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
   const int lane = tid & 63;
   const int r = lane / LPR;
   const int c = lane - r * LPR;
-  const int t0 = split * S;
-  const int b0 = t0 >> a.bs_log2;
+  const int b0s = (split * S) >> a.bs_log2;   // first table entry of the short split
+  const int b0l = (split * SL) >> a.bs_log2;  // ... and of the long one
 
-  // Issued before the context length is known, so the three loads overlap:
-  // table entries of this split (clamped to the table row), q, context length.
-  // When one block covers the whole split, its id is a single (scalar) load
-  // and no LDS staging or barrier is needed before the K/V loads.
-  constexpr bool one_block = ONE_BLOCK;
-  int blk0 = -1;
-  if constexpr (one_block) {
-    const int blk = a.block_tables[(int64_t)seq * a.mbs + b0];  // b0 < mbs for every split
-    blk0 = (blk >= 0 && blk < a.num_blocks) ? blk : -1;
+  // Issued before the context length is known, so the loads overlap: the
+  // table entries of both candidate splits (clamped to the table row), q, the
+  // context length.
+  const int32_t* trow = a.block_tables + (int64_t)seq * a.mbs;
+  auto entry = [&](int b) -> int {
+    int blk = -1;
+    if (b < a.mbs) blk = trow[b];
+    return (blk >= 0 && blk < a.num_blocks) ? blk : -1;
+  };
+  int blk_s = -1, blk_l0 = -1, blk_l1 = -1;
+  if constexpr (SCALAR_BLK) {
+    blk_s = entry(b0s);
+    if constexpr (LONG) {
+      blk_l0 = entry(b0l);
+      blk_l1 = entry(b0l + 1);
+    }
   } else {
-    const int nb_max = S >> a.bs_log2;
+    const int nbs = S >> a.bs_log2;
 #pragma unroll
     for (int k = 0; k < kMaxSplitBlocks / 256; ++k) {
       const int i = tid + 256 * k;
-      if (i < nb_max) {
-        int blk = -1;
-        if (b0 + i < a.mbs) blk = a.block_tables[(int64_t)seq * a.mbs + b0 + i];
-        s_blk[i] = (blk >= 0 && blk < a.num_blocks) ? blk : -1;
-      }
+      if (i < nbs) s_blk[i] = entry(b0s + i);
     }
   }
   // Heads past the group's end (last sub-group) re-read its last head; their
@@ -136,7 +157,9 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
   int ctx = a.context_lens[seq];
   const int cap = a.mbs << a.bs_log2;
   ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
-  const int nsplit = ctx == 0 ? 1 : (ctx + S - 1) / S;
+  const int nshort = ctx == 0 ? 1 : (ctx + S - 1) / S;
+  const bool lng = LONG && nshort > a.nsplit_max;
+  const int nsplit = lng ? (ctx + SL - 1) / SL : nshort;
 
   // APPEND: lanes 0 .. 2*NLB-1 of wave 0 write the new row (bf16, or E4M3
   // codes for KV8) into its slot when this is the sequence's last split and
@@ -172,10 +195,11 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
   // Cached tokens of this split are t0 .. t1-1 (with APPEND the last position
   // comes from k_new / v_new instead; t1 <= t0 when the split holds only it).
   // Loads past t1 re-read row `jfill`, which is in bounds and masked out.
+  const int t0 = split * (lng ? SL : S);
   const int tc = APPEND ? ctx - 1 : ctx;
-  const int t1 = min(tc, t0 + S);
+  const int t1 = min(tc, t0 + (lng ? SL : S));
   const int jfill = t1 > t0 ? t1 - 1 : t0;
-  if constexpr (!one_block) __syncthreads();  // s_blk written
+  if constexpr (!SCALAR_BLK) __syncthreads();  // s_blk written
 
   const int64_t row_stride = (int64_t)a.Hkv * D;
   const int64_t head_off = (int64_t)kvh * D + c * EPL;  // elements
@@ -229,104 +253,116 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
     }
   };
 
-  auto load_chunk = [&](int it, u32x4 (&kc)[U], u32x4 (&vc)[U], bool (&ok)[U]) {
+  // Stream the split: NI chunks per wave, DP of them in flight.  IS_LONG picks
+  // the long split's block ids.
+  auto stream = [&](auto ni_c, auto dp_c, auto long_c) {
+    constexpr int NI = decltype(ni_c)::value;
+    constexpr int DP = decltype(dp_c)::value;
+    constexpr bool IS_LONG = decltype(long_c)::value;
+    static_assert(DP >= 1 && DP <= NI, "prefetch depth");
+    const int b0 = IS_LONG ? b0l : b0s;
+    auto load_chunk = [&](int it, u32x4 (&kc)[U], u32x4 (&vc)[U], bool (&ok)[U]) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      // Rows past the split end re-read the split's last row (in bounds, finite) and
-      // are masked out of the softmax below.
-      const int j = t0 + (it * kWaves + w) * CH + u * RPW + r;
-      const int jj = j < t1 ? j : jfill;
-      int blk;
-      if constexpr (one_block) blk = blk0;
-      else blk = s_blk[(jj >> a.bs_log2) - b0];
-      ok[u] = (j < t1) && (blk >= 0);
-      blk = blk < 0 ? 0 : blk;
-      const int64_t off = (((int64_t)blk << a.bs_log2) + (jj & bs_mask)) * row_stride + head_off;
-      const u32x4* kp = (const u32x4*)((const char*)a.k_cache + off * EB);
-      const u32x4* vp = (const u32x4*)((const char*)a.v_cache + off * EB);
-      if constexpr (NT) {
-        kc[u] = __builtin_nontemporal_load(kp);
-        vc[u] = __builtin_nontemporal_load(vp);
-      } else {
-        kc[u] = *kp;
-        vc[u] = *vp;
+      for (int u = 0; u < U; ++u) {
+        // Rows past the split end re-read the split's last row (in bounds, finite) and
+        // are masked out of the softmax below.
+        const int j = t0 + (it * kWaves + w) * CH + u * RPW + r;
+        const int jj = j < t1 ? j : jfill;
+        int blk;
+        if constexpr (SCALAR_BLK) {
+          if constexpr (IS_LONG) blk = ((jj >> a.bs_log2) != b0) ? blk_l1 : blk_l0;
+          else blk = blk_s;
+        } else {
+          blk = s_blk[(jj >> a.bs_log2) - b0];
+        }
+        ok[u] = (j < t1) && (blk >= 0);
+        blk = blk < 0 ? 0 : blk;
+        const int64_t off = (((int64_t)blk << a.bs_log2) + (jj & bs_mask)) * row_stride + head_off;
+        const u32x4* kp = (const u32x4*)((const char*)a.k_cache + off * EB);
+        const u32x4* vp = (const u32x4*)((const char*)a.v_cache + off * EB);
+        if constexpr (NT) {
+          kc[u] = __builtin_nontemporal_load(kp);
+          vc[u] = __builtin_nontemporal_load(vp);
+        } else {
+          kc[u] = *kp;
+          vc[u] = *vp;
+        }
       }
-    }
-  };
+    };
 
-  // PRELOAD issues every load of the wave before the first is used; otherwise
-  // each chunk is loaded at the top of its iteration.
-  u32x4 kpre[PRELOAD ? NIT : 1][U], vpre[PRELOAD ? NIT : 1][U];
-  bool okpre[PRELOAD ? NIT : 1][U];
-  if constexpr (PRELOAD) {
+    u32x4 kpre[NI][U], vpre[NI][U];
+    bool okpre[NI][U];
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) load_chunk(it, kpre[it], vpre[it], okpre[it]);
-  }
+    for (int it = 0; it < DP; ++it) load_chunk(it, kpre[it], vpre[it], okpre[it]);
 
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    u32x4 kc[U], vc[U];
-    bool ok[U];
-    if constexpr (PRELOAD) {
+    for (int it = 0; it < NI; ++it) {
+      if (it + DP < NI) load_chunk(it + DP, kpre[it + DP], vpre[it + DP], okpre[it + DP]);
+      u32x4 kc[U], vc[U];
+      bool ok[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         kc[u] = kpre[it][u];
         vc[u] = vpre[it][u];
         ok[u] = okpre[it][u];
       }
-    } else {
-      load_chunk(it, kc, vc, ok);
-    }
 
-    float s[U][GT];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-#pragma unroll
-      for (int h = 0; h < GT; ++h) {
-        const float d = group_sum<LPR>(kdot(h, kc[u]));
-        // mul_rn: the score is rounded once and the same value is compared
-        // with and subtracted from the running max (the maximum gives p = 1).
-        s[u][h] = ok[u] ? mul_rn(d, a.scale_log2e) : -INFINITY;
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < GT; ++h) {
-      float mx = s[0][h];
-#pragma unroll
-      for (int u = 1; u < U; ++u) mx = fmaxf(mx, s[u][h]);
-      const float mnew = fmaxf(m[h], mx);
-      const float alpha = __builtin_amdgcn_exp2f(m[h] - mnew);
-      m[h] = mnew;
-      float psum = 0.f;
+      float s[U][GT];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        s[u][h] = __builtin_amdgcn_exp2f(s[u][h] - mnew);
-        psum += s[u][h];
+#pragma unroll
+        for (int h = 0; h < GT; ++h) {
+          const float d = group_sum<LPR>(kdot(h, kc[u]));
+          // mul_rn: the score is rounded once and the same value is compared
+          // with and subtracted from the running max (the maximum gives p = 1).
+          s[u][h] = ok[u] ? mul_rn(d, a.scale_log2e) : -INFINITY;
+        }
       }
-      l[h] = l[h] * alpha + psum;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      // Masked rows contribute p = 0; zeroing V as well keeps a NaN in an
-      // unused slot from turning 0 * NaN into NaN.
-      // (Selected per component: a select of the whole vector makes the
-      // compiler keep extra copies of the preloaded rows live.)
-      u32x4 vm;
-      vm.x = ok[u] ? vc[u].x : 0u;
-      vm.y = ok[u] ? vc[u].y : 0u;
-      vm.z = ok[u] ? vc[u].z : 0u;
-      vm.w = ok[u] ? vc[u].w : 0u;
-      float vf[EPL];
-      vconv(vm, vf);
 #pragma unroll
       for (int h = 0; h < GT; ++h) {
+        float mx = s[0][h];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(s[u][h], vf[e], acc[h][e]);
+        for (int u = 1; u < U; ++u) mx = fmaxf(mx, s[u][h]);
+        const float mnew = fmaxf(m[h], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m[h] - mnew);
+        m[h] = mnew;
+        float psum = 0.f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          s[u][h] = __builtin_amdgcn_exp2f(s[u][h] - mnew);
+          psum += s[u][h];
+        }
+        l[h] = l[h] * alpha + psum;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        // Masked rows contribute p = 0; zeroing V as well keeps a NaN in an
+        // unused slot from turning 0 * NaN into NaN.
+        // (Selected per component: a select of the whole vector makes the
+        // compiler keep extra copies of the preloaded rows live.)
+        u32x4 vm;
+        vm.x = ok[u] ? vc[u].x : 0u;
+        vm.y = ok[u] ? vc[u].y : 0u;
+        vm.z = ok[u] ? vc[u].z : 0u;
+        vm.w = ok[u] ? vc[u].w : 0u;
+        float vf[EPL];
+        vconv(vm, vf);
+#pragma unroll
+        for (int h = 0; h < GT; ++h) {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(s[u][h], vf[e], acc[h][e]);
+        }
       }
     }
-  }
+  };
+  using std_false = std::integral_constant<bool, false>;
+  using std_true = std::integral_constant<bool, true>;
+  if (LONG && lng)
+    stream(std::integral_constant<int, 2 * NIT>{}, std::integral_constant<int, DEPTH_LONG>{}, std_true{});
+  else
+    stream(std::integral_constant<int, NIT>{}, std::integral_constant<int, DEPTH>{}, std_false{});
 
   // APPEND: row slot 0 of wave 0 takes the new token (last split only).
   if constexpr (APPEND) {
@@ -431,6 +467,12 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
   }
 }
 
+template <int D, int GT, int U, int NIT, int DEPTH, int DEPTH_LONG, bool LONG, bool NT, bool KV8,
+          bool APPEND, bool SCALAR_BLK>
+__global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
+  paged_decode_body<D, GT, U, NIT, DEPTH, DEPTH_LONG, LONG, NT, KV8, APPEND, SCALAR_BLK>(a);
+}
+
 // Merge the split-K partials of one (sequence, head group):
 // out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), M = max_s m_s, in split order.
 // The partial outputs of the first kCombineChunk splits and every split's
@@ -485,7 +527,8 @@ __global__ __launch_bounds__(256) void paged_decode_combine_kernel(DecodeArgs a)
   int ctx = a.context_lens[seq];
   const int cap = a.mbs << a.bs_log2;
   ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
-  const int nsplit = (ctx + S - 1) / S;
+  int nsplit = (ctx + S - 1) / S;
+  if (a.long_splits && nsplit > a.nsplit_max) nsplit = (ctx + 2 * S - 1) / (2 * S);
   if (nsplit <= 1) return;  // written directly by the main kernel
   const int kvh = hg / a.nsub;
   const int sub = hg - kvh * a.nsub;
@@ -534,15 +577,16 @@ __global__ __launch_bounds__(256) void paged_decode_combine_kernel(DecodeArgs a)
 }
 
 // Production tiling (measured on the Qwen3-0.6B-shaped decode, 64 x 16/8 heads,
-// contexts up to 4096): every load issued up front, non-temporal (streaming)
-// loads.  bf16: U = 2 rows per lane per chunk, NIT = 8 chunks per wave; FP8:
-// U = 2, NIT = 4 (a 16-byte load carries twice the elements).  Either way a
-// split is 256 tokens at D = 128 and 512 tokens at D = 64.
-constexpr bool kPreload = true;
+// contexts up to 4096): non-temporal (streaming) loads; a short split issues
+// every load up front, a long split keeps as many chunks in flight.  bf16:
+// U = 2 rows per lane per chunk, NIT = 8 chunks per wave; FP8: U = 2, NIT = 4
+// (a 16-byte load carries twice the elements).  Either way a short split is
+// 256 tokens at D = 128 and 512 tokens at D = 64.
 constexpr bool kNontemporal = true;
 
 template <bool KV8> constexpr int tile_u() { return 2; }
 template <bool KV8> constexpr int tile_nit() { return KV8 ? 4 : 8; }
+template <bool KV8> constexpr int tile_depth() { return tile_nit<KV8>(); }
 template <bool KV8> constexpr int max_gt() { return KV8 ? 4 : 8; }
 
 template <int D, bool KV8>
@@ -550,17 +594,25 @@ constexpr int split_tokens() {
   return kWaves * tile_nit<KV8>() * tile_u<KV8>() * (64 / (D / (KV8 ? 16 : 8)));
 }
 
+template <int D, int GT, bool KV8, bool APPEND, bool LONG, bool SCALAR_BLK>
+void launch_main(const DecodeArgs& a, unsigned nwg, hipStream_t stream) {
+  hipLaunchKernelGGL((paged_decode_kernel<D, GT, tile_u<KV8>(), tile_nit<KV8>(), tile_depth<KV8>(),
+                                          tile_depth<KV8>() / 4, LONG, kNontemporal, KV8, APPEND,
+                                          SCALAR_BLK>),
+                     dim3(nwg), dim3(256), 0, stream, a);
+}
+
 template <int D, int GT, bool KV8, bool APPEND>
 int launch_d(const DecodeArgs& a, int B, hipStream_t stream) {
-  const int64_t nwg = (int64_t)B * a.hg * a.nsplit_max;
-  if ((1 << a.bs_log2) >= split_tokens<D, KV8>())
-    hipLaunchKernelGGL((paged_decode_kernel<D, GT, tile_u<KV8>(), tile_nit<KV8>(), kPreload,
-                                            kNontemporal, KV8, APPEND, true>),
-                       dim3((unsigned)nwg), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((paged_decode_kernel<D, GT, tile_u<KV8>(), tile_nit<KV8>(), kPreload,
-                                            kNontemporal, KV8, APPEND, false>),
-                       dim3((unsigned)nwg), dim3(256), 0, stream, a);
+  const unsigned nwg = (unsigned)((int64_t)B * a.hg * a.nsplit_max);
+  const bool scalar_blk = (1 << a.bs_log2) >= split_tokens<D, KV8>();
+  if (a.long_splits) {  // planned only when a block holds a short split
+    if (!scalar_blk) return -2;
+    launch_main<D, GT, KV8, APPEND, true, true>(a, nwg, stream);
+  } else {
+    if (scalar_blk) launch_main<D, GT, KV8, APPEND, false, true>(a, nwg, stream);
+    else launch_main<D, GT, KV8, APPEND, false, false>(a, nwg, stream);
+  }
   if (hipGetLastError() != hipSuccess) return -1;
   if (a.nsplit_max > 1) {
     hipLaunchKernelGGL((paged_decode_combine_kernel<D, GT, split_tokens<D, KV8>()>),
@@ -612,8 +664,17 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int head_dim, int block_size, int
   int sl = 0;
   while ((1 << sl) < S) ++sl;
   p.split_log2 = sl;
-  p.nsplit_max = (int)((max_ctx + S - 1) / S);
-  if (p.nsplit_max < 1) p.nsplit_max = 1;
+  p.nsplit_short = (int)((max_ctx + S - 1) / S);
+  if (p.nsplit_short < 1) p.nsplit_short = 1;
+  // Long splits halve the grid's slots per sequence.  They are taken only
+  // when a cache block holds a whole short split (the block ids stay scalar
+  // loads), the longest context needs many short splits, and the halved grid
+  // still gives every compute unit many workgroups (coarser work items make
+  // the end of a small grid ragged).
+  const int64_t half = (p.nsplit_short + 1) / 2;
+  p.long_splits = block_size >= S && p.nsplit_short >= kLongSplitMinShort &&
+                  units * half >= kLongSplitMinGrid;
+  p.nsplit_max = p.long_splits ? (int)half : p.nsplit_short;
   const int64_t parts = units * p.nsplit_max * p.gt;
   auto round256 = [](size_t x) { return (x + 255) / 256 * 256; };
   p.units = units;

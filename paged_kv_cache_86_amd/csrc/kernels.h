@@ -11,8 +11,15 @@ constexpr float kLog2eHost = 1.4426950408889634f;
 // Upper bound of (sequence, KV-head group) pairs in one decode call (one
 // combine workgroup each).
 constexpr int64_t kDecodeMaxUnits = 1 << 24;
-// Most splits one decode context may span (the merge stages them in LDS).
+// Most short splits one decode context may span (bounds the longest context;
+// the merge stages up to this many partials in LDS).
 constexpr int kDecodeMaxSplits = 256;
+// Long splits (twice the short length) are used when the longest context
+// spans at least this many short splits ...
+constexpr int kLongSplitMinShort = 8;
+// ... and the grid with half the slots per sequence still has this many
+// workgroups (32 per compute unit of a 256-CU device).
+constexpr int64_t kLongSplitMinGrid = 8192;
 
 int launch_kvcache_store(const void* k, const void* v, const int32_t* slot_mapping, int T,
                          void* k_cache, void* v_cache, int num_blocks, int block_size,
@@ -28,8 +35,10 @@ struct DecodePlan {
   int group;       // query heads per KV head
   int nsub;        // workgroups sharing one KV head's query heads
   int gt;          // query heads handled by one workgroup (<= 8)
-  int split_log2;  // tokens per split = 1 << split_log2
-  int nsplit_max;  // splits of the longest possible context
+  int split_log2;    // tokens per short split = 1 << split_log2
+  int nsplit_short;  // short splits of the longest possible context
+  bool long_splits;  // contexts above nsplit_max short splits use splits of twice the length
+  int nsplit_max;    // workgroups (and partial slots) per (sequence, head group)
   int64_t units;   // (sequence, head group) pairs
   size_t ml_bytes, o_bytes;  // workspace regions: (max, sum) pairs, then unnormalised outputs
   size_t workspace_bytes() const { return ml_bytes + o_bytes; }
@@ -48,6 +57,7 @@ struct DecodeArgs {
   float* ws_ml;
   float* ws_o;
   int mbs, Hq, Hkv, group, nsub, hg, bs_log2, split_log2, nsplit_max, num_blocks, out_f32;
+  int long_splits;    // see DecodePlan
   float scale_log2e;  // softmax scale (times the K scale of an FP8 cache) times log2(e)
   float v_scale;      // V scale of an FP8 cache (1 for bf16)
   // Fused store of the new token (append variants only; unused otherwise).

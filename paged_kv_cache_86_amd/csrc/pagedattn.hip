@@ -76,7 +76,7 @@ size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, i
     return 0;
   const pa::DecodePlan p = pa::plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                            block_size, max_blocks_per_seq, kv8);
-  return (p.units > pa::kDecodeMaxUnits || p.nsplit_max > pa::kDecodeMaxSplits)
+  return (p.units > pa::kDecodeMaxUnits || p.nsplit_short > pa::kDecodeMaxSplits)
              ? 0
              : p.workspace_bytes();
 }
@@ -115,7 +115,7 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   const int64_t hg = (int64_t)num_kv_heads * p.nsub;
   if ((int64_t)num_seqs * hg * p.nsplit_max > INT32_MAX) return PA_ERR_SHAPE;
   if (p.units > pa::kDecodeMaxUnits) return PA_ERR_SHAPE;
-  if (p.nsplit_max > pa::kDecodeMaxSplits) return PA_ERR_UNSUPPORTED;
+  if (p.nsplit_short > pa::kDecodeMaxSplits) return PA_ERR_UNSUPPORTED;
 
   pa::DecodeArgs a{};
   a.q = (const uint16_t*)q;
@@ -136,6 +136,7 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   a.bs_log2 = bs_log2;
   a.split_log2 = p.split_log2;
   a.nsplit_max = p.nsplit_max;
+  a.long_splits = p.long_splits;
   a.num_blocks = num_blocks;
   a.out_f32 = out_dtype == PA_F32;
   const float sc = resolve_scale(scale, head_dim);

@@ -88,6 +88,11 @@ def test_decode_workspace_sizes():
     b = pa.decode_workspace_bytes(64, 16, 8, 128, 256, 16)
     assert b == 64 * 8 * 16 * 2 * 2 * 4 + 64 * 8 * 16 * 2 * 128 * 4
     assert pa.decode_workspace_bytes(0, 16, 8, 128, 256, 16) == 0
+    # 128 x 8 head groups x 8 slots reach 8192 workgroups: splits of 512 tokens for contexts
+    # above 8 x 256, so 8 partial slots per head group instead of 16
+    assert pa.decode_workspace_bytes(128, 16, 8, 128, 256, 16) == 128 * 8 * 8 * 2 * (2 + 128) * 4
+    # with blocks smaller than a split the block ids stay in LDS: short splits only
+    assert pa.decode_workspace_bytes(128, 16, 8, 128, 16, 256) == 128 * 8 * 16 * 2 * (2 + 128) * 4
     assert pa.decode_workspace_bytes(4, 6, 4, 128, 16, 8) == 0  # 6 % 4 != 0
     assert pa.decode_workspace_bytes(4, 8, 4, 128, 16, 4097) == 0  # context above 65536 tokens
     # more query heads per KV head than one workgroup serves: split into sub-groups

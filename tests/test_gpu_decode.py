@@ -249,3 +249,36 @@ def test_decode_append_small_cases(case):
         if n == 1:  # the only key is the appended token: out = v_new exactly
             for h in range(Hq):
                 assert np.array_equal(out32[i, h], oracle.bf16_to_f64(c.v_new[i, h // G]))
+
+
+def _long_split_case(seed, D, BS, B=128):
+    """B x 16/8 heads, blocks holding a whole split: a grid big enough for splits of twice the
+    length; contexts at every split-length boundary of both kinds, the rest drawn uniformly."""
+    S = 256 if D == 128 else 512  # short split length
+    edges = [1, 2, S - 1, S, S + 1, 8 * S - 1, 8 * S, 8 * S + 1, 9 * S, 9 * S + 1, 10 * S - 1,
+             16 * S - 1, 16 * S, 0, 2 * S, 2 * S + 1]
+    rng = np.random.default_rng(seed)
+    ctx = edges + [int(x) for x in rng.integers(1, 16 * S, B - len(edges), endpoint=True)]
+    return decode_case(seed, ctx, 16, 8, D, BS, nb_factor=1.2, max_blocks_per_seq=16 * S // BS)
+
+
+@pytest.mark.parametrize("D,BS", [(128, 256), (128, 1024), (64, 512)])
+def test_decode_long_splits(D, BS):
+    """Contexts longer than the grid's short-split slots take splits of twice the length (over
+    two blocks or inside one): every sequence (both split kinds and every boundary) against the
+    oracle, plain and fused store."""
+    dev = device()
+    c = _long_split_case(4321 + D + BS, D, BS)
+    B, P = c.batch, 8
+    parts = B * 8 * P * 2  # (sequence, KV head) x slots x query heads per workgroup
+    assert pa.decode_workspace_bytes(B, 16, 8, D, BS, c.max_blocks_per_seq) == parts * (2 + D) * 4
+    say(f"[decode-long] D={D} BS={BS} B={B} ctx max {int(c.context_lens.max())}")
+    d = DecodeOnDevice(c, dev)
+    d.store()
+    out32 = as_f64(d.decode(torch.float32))
+    kc, vc = oracle.kvcache_store(c.k_new, c.v_new, c.slot_mapping, c.k_cache, c.v_cache)
+    ref = oracle.paged_decode(c.q, kc, vc, c.block_tables, c.context_lens, np.float32(c.scale))
+    err = np.abs(out32 - ref).max()
+    say(f"[decode-long] D={D} BS={BS}: max|err| {err:.3e}")
+    assert err <= ATOL
+    check_append(c, dev, f"long splits D{D} BS{BS}")

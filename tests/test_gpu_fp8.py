@@ -254,3 +254,39 @@ def test_decode_append_fp8(case):
             vrow = np.float32(oracle.e4m3_decode(vc8[blk, off]) * np.float32(vs))
             for h in range(Hq):
                 assert np.array_equal(got[i, h], vrow[h // G].astype(np.float64))
+
+
+def test_decode_fp8_long_splits():
+    """128 x 16/8 heads at block 256: contexts above 8 short splits take splits of 512 tokens
+    (both kinds and every boundary) on an FP8 pool, plain and fused store."""
+    dev = device()
+    S = 256
+    edges = [1, 2, S - 1, S, S + 1, 8 * S - 1, 8 * S, 8 * S + 1, 9 * S, 9 * S + 1, 16 * S - 1,
+             16 * S, 0, 2 * S + 1]
+    rng = np.random.default_rng(4444)
+    ctx = edges + [int(x) for x in rng.integers(1, 16 * S, 128 - len(edges), endpoint=True)]
+    c = decode_case(4444, ctx, 16, 8, 128, 256, nb_factor=1.2, max_blocks_per_seq=16)
+    assert pa.decode_fp8_workspace_bytes(128, 16, 8, 128, 256, 16) == 128 * 8 * 8 * 2 * 130 * 4
+    say(f"[fp8-long] B=128 ctx max {int(c.context_lens.max())}")
+    check_decode(Fp8Pool(c, dev, 0.0125, 0.02), label="long splits")
+    ks, vs = 0.0125, 0.02
+    NB = c.k_cache.shape[0]
+    kc = torch.empty((NB, 256, 8, 128), dtype=torch.uint8, device=dev)
+    vc = torch.empty_like(kc)
+    every = np.arange(NB * 256, dtype=np.int32)
+    pa.kvcache_store_fp8(bf16(c.k_cache.reshape(NB * 256, 8, 128), dev),
+                         bf16(c.v_cache.reshape(NB * 256, 8, 128), dev), i32(every, dev), kc, vc,
+                         ks, vs)
+    out = torch.empty((128, 16, 128), dtype=torch.float32, device=dev)
+    pa.paged_decode_append_fp8(bf16(c.q, dev), bf16(c.k_new, dev), bf16(c.v_new, dev),
+                               i32(c.slot_mapping, dev), kc, vc, i32(c.block_tables, dev),
+                               i32(c.context_lens, dev), c.scale, ks, vs, out)
+    kc8, vc8 = oracle.kvcache_store_fp8(c.k_new, c.v_new, c.slot_mapping,
+                                        oracle.quantize(c.k_cache, ks),
+                                        oracle.quantize(c.v_cache, vs), ks, vs)
+    assert np.array_equal(codes(kc), kc8) and np.array_equal(codes(vc), vc8)
+    ref = oracle.paged_decode_fp8(c.q, kc8, vc8, c.block_tables, c.context_lens,
+                                  np.float32(c.scale), ks, vs)
+    err = np.abs(as_f64(out) - ref).max()
+    say(f"[fp8-long] fused store: max|err| {err:.3e}")
+    assert err <= ATOL

@@ -481,8 +481,9 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeArgs a) {
 // kCombineChunk splits the merge costs one memory round trip.
 constexpr int kCombineChunk = 16;
 
-template <int D, int GT, int S>
+template <int D, int GT>
 __global__ __launch_bounds__(256) void paged_decode_combine_kernel(DecodeArgs a) {
+  const int S = 1 << a.split_log2;  // tokens per (short) split
   constexpr int ITEMS = (GT * D + 255) / 256;  // (head, dim) outputs per thread
   __shared__ float s_w[kDecodeMaxSplits][GT];  // per split: 2^(m_s - M) / L
   const int unit = blockIdx.x;
@@ -614,12 +615,37 @@ int launch_d(const DecodeArgs& a, int B, hipStream_t stream) {
     else launch_main<D, GT, KV8, APPEND, false, false>(a, nwg, stream);
   }
   if (hipGetLastError() != hipSuccess) return -1;
-  if (a.nsplit_max > 1) {
-    hipLaunchKernelGGL((paged_decode_combine_kernel<D, GT, split_tokens<D, KV8>()>),
-                       dim3((unsigned)((int64_t)B * a.hg)), dim3(256), 0, stream, a);
-    if (hipGetLastError() != hipSuccess) return -1;
+  return a.nsplit_max > 1 ? launch_decode_combine(a, B, D, GT, stream) : 0;
+}
+
+template <int D, int GT>
+int launch_combine(const DecodeArgs& a, int B, hipStream_t stream) {
+  hipLaunchKernelGGL((paged_decode_combine_kernel<D, GT>), dim3((unsigned)((int64_t)B * a.hg)),
+                     dim3(256), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+template <int D>
+int launch_combine_d(const DecodeArgs& a, int B, int gt, hipStream_t stream) {
+  switch (gt) {
+    case 1: return launch_combine<D, 1>(a, B, stream);
+    case 2: return launch_combine<D, 2>(a, B, stream);
+    case 3: return launch_combine<D, 3>(a, B, stream);
+    case 4: return launch_combine<D, 4>(a, B, stream);
+    case 5: return launch_combine<D, 5>(a, B, stream);
+    case 6: return launch_combine<D, 6>(a, B, stream);
+    case 7: return launch_combine<D, 7>(a, B, stream);
+    case 8: return launch_combine<D, 8>(a, B, stream);
+    case 9: return launch_combine<D, 9>(a, B, stream);
+    case 10: return launch_combine<D, 10>(a, B, stream);
+    case 11: return launch_combine<D, 11>(a, B, stream);
+    case 12: return launch_combine<D, 12>(a, B, stream);
+    case 13: return launch_combine<D, 13>(a, B, stream);
+    case 14: return launch_combine<D, 14>(a, B, stream);
+    case 15: return launch_combine<D, 15>(a, B, stream);
+    case 16: return launch_combine<D, 16>(a, B, stream);
   }
-  return 0;
+  return -2;
 }
 
 template <int D, bool KV8, bool APPEND>
@@ -651,16 +677,26 @@ int launch_head_dim(const DecodeArgs& a, int B, int head_dim, int gt, hipStream_
 
 }  // namespace
 
+int launch_decode_combine(const DecodeArgs& a, int B, int head_dim, int gt, hipStream_t stream) {
+  if (head_dim == 128) return launch_combine_d<128>(a, B, gt, stream);
+  if (head_dim == 64) return launch_combine_d<64>(a, B, gt, stream);
+  return -2;
+}
+
 DecodePlan plan_decode(int B, int Hq, int Hkv, int head_dim, int block_size, int mbs, bool kv8) {
   DecodePlan p{};
-  const int gmax = kv8 ? max_gt<true>() : max_gt<false>();
   p.group = Hq / Hkv;
+  // Groups of kMfmaMinGroup or more query heads per KV head run the MFMA
+  // kernel (bf16 pools): the VALU kernel's vector work grows with the group.
+  p.mfma = !kv8 && p.group >= kMfmaMinGroup;
+  const int gmax = p.mfma ? kMfmaMaxGt : (kv8 ? max_gt<true>() : max_gt<false>());
   p.nsub = (p.group + gmax - 1) / gmax;
   p.gt = (p.group + p.nsub - 1) / p.nsub;
   const int64_t max_ctx = (int64_t)mbs * block_size;
   const int64_t units = (int64_t)B * Hkv * p.nsub;
-  const int S = head_dim == 64 ? (kv8 ? split_tokens<64, true>() : split_tokens<64, false>())
-                               : (kv8 ? split_tokens<128, true>() : split_tokens<128, false>());
+  const int S = p.mfma ? kMfmaSplitTokens
+                : head_dim == 64 ? (kv8 ? split_tokens<64, true>() : split_tokens<64, false>())
+                                 : (kv8 ? split_tokens<128, true>() : split_tokens<128, false>());
   int sl = 0;
   while ((1 << sl) < S) ++sl;
   p.split_log2 = sl;
@@ -672,7 +708,7 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int head_dim, int block_size, int
   // still gives every compute unit many workgroups (coarser work items make
   // the end of a small grid ragged).
   const int64_t half = (p.nsplit_short + 1) / 2;
-  p.long_splits = block_size >= S && p.nsplit_short >= kLongSplitMinShort &&
+  p.long_splits = !p.mfma && block_size >= S && p.nsplit_short >= kLongSplitMinShort &&
                   units * half >= kLongSplitMinGrid;
   p.nsplit_max = p.long_splits ? (int)half : p.nsplit_short;
   const int64_t parts = units * p.nsplit_max * p.gt;
@@ -684,8 +720,9 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int head_dim, int block_size, int
 }
 
 int launch_paged_decode(const DecodeArgs& a, int B, int head_dim, int gt, bool kv8, bool append,
-                        hipStream_t stream) {
+                        bool mfma, hipStream_t stream) {
   if (B == 0) return 0;
+  if (mfma) return kv8 ? -2 : launch_paged_decode_mfma(a, B, head_dim, append, stream);
   if (kv8) {
     return append ? launch_head_dim<true, true>(a, B, head_dim, gt, stream)
                   : launch_head_dim<true, false>(a, B, head_dim, gt, stream);

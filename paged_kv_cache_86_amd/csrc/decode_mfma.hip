@@ -1,0 +1,418 @@
+// Paged decode on bf16 MFMA for large query-head groups (GQA), gfx950.
+//
+// Same operation, split-K decomposition and partial layout as the VALU decode
+// kernel (MinivLLM guide "vLLM 技术路线", Step 4 §4.5-4.6; "Nano-vLLM源码学习(2)"
+// §2): one workgroup per (sequence, KV head [sub-group], split), partials
+// merged by the same combine kernel.  What changes is the arithmetic: with G
+// query heads per KV head the VALU kernel spends about 2.7 G vector operations
+// per K/V element, which for G >= 4 is more than the vector units can retire
+// at HBM speed, so here both contractions of a split run on
+// v_mfma_f32_16x16x32_bf16 with the G heads as one 16-wide operand side:
+//
+//   * S^T = K Q^T per 16-key tile: the K operand (16 keys x 32 dims) is loaded
+//     straight from the cache into registers, 16 bytes per lane; Q^T sits in
+//     registers for the whole split (heads past G are zero);
+//   * the softmax is per lane: lane l holds query head l % 16 and four keys of
+//     each tile, and the row max takes two exchanges;
+//   * O^T = V^T P^T: P^T comes from the S^T registers (bf16), the V^T operand
+//     needs V transposed, so each wave writes its V rows into a private LDS
+//     area (16-byte chunks XOR-swizzled by row) and reads them back with
+//     ds_read_b64_tr_b16; the 32 keys of a chunk map to the MFMA's 32
+//     contraction slots in the same (permuted) order on both operands;
+//   * the softmax denominator is a third MFMA of P^T against ones, so it sums
+//     exactly the bf16 weights the PV product uses.
+//
+// Masked keys (past the split's last cached token, or in a block the table
+// does not map) get score -inf and read the query head's row instead of the
+// cache, so that p = 0 multiplies finite values.
+#include "common.h"
+#include "kernels.h"
+
+namespace pa {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kW = 4;             // waves per workgroup
+constexpr int kCK = 32;           // keys per wave chunk: two 16-key MFMA tiles
+constexpr int kMaxSplitIds = 512; // staged block ids of one split
+constexpr int kQR = 16;           // query heads per workgroup (one MFMA side)
+
+__device__ __forceinline__ f32x4_t mfma16(const u32x4& a, const u32x4& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{lo, hi}, bf16x2_t));
+}
+
+// 16-byte chunk position of chunk c of staged V row r (XOR swizzle over the
+// row's chunks, so the row-wise writes and the transposing reads both spread
+// over the LDS banks).
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (r >> 1) & 7;
+}
+
+// One workgroup = one (sequence, head sub-group, split of S = kW * NCH * kCK
+// tokens); wave w takes chunks w, w + 4, ...  DEPTH chunks of K and V are in
+// flight per wave.
+template <int D, int NCH, int DEPTH, bool APPEND, bool SCALAR_BLK>
+__global__ __launch_bounds__(256) void paged_decode_mfma_kernel(DecodeArgs a) {
+  constexpr int KS = D / 32;           // 32-dim contraction steps of S^T
+  constexpr int DT = D / 16;           // 16-dim tiles of O^T
+  constexpr int LPR = D / 8;           // lanes per V row (16-byte chunks)
+  constexpr int RPI = 64 / LPR;        // V rows per 64-lane load
+  constexpr int NVL = kCK / RPI;       // V loads per lane per chunk
+  constexpr int S = kW * NCH * kCK;    // tokens per split
+  constexpr int VROW = D * 2;          // bytes of a staged V row
+  constexpr int VAREA = kCK * VROW;    // bytes of one wave's V area
+  constexpr int NLB = D / 8;           // 16-byte vectors of a new K (or V) row
+  static_assert(DEPTH >= 1 && DEPTH <= NCH, "prefetch depth");
+  static_assert(kW * VAREA >= kW * kQR * D * 4, "the V areas hold the merge");
+
+  // V staging during the loop; the per-wave (m, l, O) for the merge afterwards.
+  __shared__ __align__(16) char s_v[kW * VAREA];
+  __shared__ int s_blk[SCALAR_BLK ? 1 : kMaxSplitIds];
+  __shared__ float s_m[kW][kQR];
+  __shared__ float s_l[kW][kQR];
+
+  const int bid = blockIdx.x;
+  const int hg = bid % a.hg;
+  const int rest = bid / a.hg;
+  const int split = rest % a.nsplit_max;
+  const int seq = rest / a.nsplit_max;
+  const int kvh = hg / a.nsub;
+  const int sub = hg - kvh * a.nsub;
+  const int gt = (a.group + a.nsub - 1) / a.nsub;  // heads per sub-group (partial stride)
+  const int h0 = kvh * a.group + sub * gt;
+  const int gh = min(gt, a.group - sub * gt);
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int qr = lane & 15;   // this lane's query head (MFMA column)
+  const int g = lane >> 4;    // this lane's 8-slot group of the contraction
+  const int t0 = split * S;
+  const int b0 = t0 >> a.bs_log2;
+  const int32_t* trow = a.block_tables + (int64_t)seq * a.mbs;
+
+  // Issued before the context length is known: block ids, q, the new token.
+  int blk0 = -1;
+  if constexpr (SCALAR_BLK) {
+    const int b = b0 < a.mbs ? trow[b0] : -1;
+    blk0 = (b >= 0 && b < a.num_blocks) ? b : -1;
+  } else {
+    const int nb = S >> a.bs_log2;
+#pragma unroll
+    for (int k = 0; k < kMaxSplitIds / 256; ++k) {
+      const int i = tid + 256 * k;
+      if (i < nb) {
+        const int b = b0 + i < a.mbs ? trow[b0 + i] : -1;
+        s_blk[i] = (b >= 0 && b < a.num_blocks) ? b : -1;
+      }
+    }
+  }
+  // Q^T operand of step ks: dims 32 ks + 8 g .. + 7 of head h0 + qr (zero past the group).
+  const uint16_t* qhead = a.q + ((int64_t)seq * a.Hq + h0 + min(qr, gh - 1)) * D;
+  u32x4 qb[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const u32x4 v = *(const u32x4*)(qhead + 32 * ks + 8 * g);
+    qb[ks] = qr < gh ? v : u32x4{0u, 0u, 0u, 0u};
+  }
+  const bool new_lane = APPEND && tid < 2 * NLB;
+  const bool new_is_v = tid >= NLB;
+  const int new_c = new_is_v ? tid - NLB : tid;
+  u32x4 xnew{};
+  int slot = -1;
+  if constexpr (APPEND) {
+    if (new_lane) {
+      const uint16_t* src = new_is_v ? a.v_new : a.k_new;
+      xnew = *(const u32x4*)(src + ((int64_t)seq * a.Hkv + kvh) * D + new_c * 8);
+      slot = a.slot_mapping[seq];
+    }
+  }
+  int ctx = a.context_lens[seq];
+  const int cap = a.mbs << a.bs_log2;
+  ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
+  const int nsplit = ctx == 0 ? 1 : (ctx + S - 1) / S;
+
+  auto store_new = [&]() {
+    if (new_lane && sub == 0 && slot >= 0 && (int64_t)slot < a.num_slots) {
+      const int64_t dst = ((int64_t)slot * a.Hkv + kvh) * D + new_c * 8;
+      *(u32x4*)((uint16_t*)(new_is_v ? a.v_cache_w : a.k_cache_w) + dst) = xnew;
+    }
+  };
+  if (ctx == 0) {  // padded row: output zeros
+    if constexpr (APPEND) {
+      if (split == 0 && w == 0) store_new();
+    }
+    if (split == 0) {
+      for (int i = tid; i < gh * D; i += blockDim.x) {
+        const int64_t o = ((int64_t)seq * a.Hq + h0) * D + i;
+        if (a.out_f32) ((float*)a.out)[o] = 0.f;
+        else ((uint16_t*)a.out)[o] = 0;
+      }
+    }
+    return;
+  }
+  if (split >= nsplit) return;
+  // Cached tokens of this split: t0 .. t1-1 (with APPEND position ctx-1 comes
+  // from k_new / v_new, and its cache row may not be written yet).  Keys past
+  // t1 are masked out and read the query head instead (finite).
+  const int tc = APPEND ? ctx - 1 : ctx;
+  const int t1 = min(tc, t0 + S);
+  if constexpr (!SCALAR_BLK) __syncthreads();  // s_blk written
+
+  const int64_t row_stride = (int64_t)a.Hkv * D;
+  const int bs_mask = (1 << a.bs_log2) - 1;
+  // Element offset of key j's row of this KV head, or -1 when its block is unmapped.
+  auto row_of = [&](int j) -> int64_t {
+    const int blk = SCALAR_BLK ? blk0 : s_blk[(j >> a.bs_log2) - b0];
+    if (blk < 0) return -1;
+    return (((int64_t)blk << a.bs_log2) + (j & bs_mask)) * row_stride + (int64_t)kvh * D;
+  };
+  // Unmapped rows are read from the query head instead (finite; masked out).
+  auto kv_ptr = [&](const uint16_t* base, int64_t row, int elem) -> const u32x4* {
+    return (const u32x4*)(row >= 0 ? base + row + elem : qhead + elem);
+  };
+
+  char* vmine = s_v + w * VAREA;
+  // LDS byte offsets of this lane's V row chunk writes, and of its transposing
+  // reads: read rd of tile dt returns column 16 dt + qr at keys 16 rd + 4 g .. + 3.
+  int vw_off[NVL];
+#pragma unroll
+  for (int i = 0; i < NVL; ++i) {
+    const int r = i * RPI + lane / LPR;
+    vw_off[i] = r * VROW + (((lane % LPR) ^ vswz<D>(r)) * 16);
+  }
+  int vr_off[DT][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      const int r = 16 * rd + 4 * g + (qr >> 2);
+      const int dcol = 16 * dt + 4 * (qr & 3);
+      vr_off[dt][rd] = r * VROW + (((dcol >> 3) ^ vswz<D>(r)) * 16) + (dcol & 7) * 2;
+    }
+  }
+
+  struct Chunk {
+    u32x4 k[2][KS];  // K operand: keys 16 kt + qr, dims 32 ks + 8 g .. + 7
+    u32x4 v[NVL];    // V rows i * RPI + lane / LPR, chunk lane % LPR
+  };
+  auto load_chunk = [&](int it, Chunk& ch) {
+    const int k0 = t0 + (it * kW + w) * kCK;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int j = k0 + 16 * kt + qr;
+      const int64_t row = j < t1 ? row_of(j) : -1;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        ch.k[kt][ks] = __builtin_nontemporal_load(kv_ptr(a.k_cache, row, 32 * ks + 8 * g));
+    }
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) {
+      const int j = k0 + i * RPI + lane / LPR;
+      const int64_t row = j < t1 ? row_of(j) : -1;
+      ch.v[i] = __builtin_nontemporal_load(kv_ptr(a.v_cache, row, (lane % LPR) * 8));
+    }
+  };
+
+  f32x4_t oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t lacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = kNegBig;  // running max (log2 units) of this lane's query head
+  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0
+
+  auto compute_chunk = [&](int it, const Chunk& ch) {
+    const int k0 = t0 + (it * kW + w) * kCK;
+    f32x4_t sacc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      sacc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) sacc[kt] = mfma16(ch.k[kt][ks], qb[ks], sacc[kt]);
+    }
+    // V rows into this wave's LDS area (read back transposed below).
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) *(u32x4*)(vmine + vw_off[i]) = ch.v[i];
+    // Scores of keys k0 + 16 kt + 4 g + e (log2 units), masked to -inf.
+    float s[2][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = k0 + 16 * kt + 4 * g + e;
+        bool ok = j < t1;
+        if constexpr (SCALAR_BLK) ok = ok && blk0 >= 0;
+        else ok = ok && s_blk[(j >> a.bs_log2) - b0] >= 0;
+        s[kt][e] = ok ? mul_rn(sacc[kt][e], a.scale_log2e) : -INFINITY;
+        mx = fmaxf(mx, s[kt][e]);
+      }
+    }
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const float mnew = fmaxf(m, mx);
+    if (__builtin_amdgcn_ballot_w64(mnew > m) != 0) {  // alpha == 1 exactly otherwise
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+      lacc *= alpha;
+      m = mnew;
+    }
+    // P^T operand: contraction slots 8 g .. 8 g + 3 are keys 4 g .. + 3 of tile 0,
+    // slots 8 g + 4 .. + 7 keys 16 + 4 g .. + 3 (tile 1).
+    const u32x4 pb = {
+        pack_bf16(__builtin_amdgcn_exp2f(s[0][0] - m), __builtin_amdgcn_exp2f(s[0][1] - m)),
+        pack_bf16(__builtin_amdgcn_exp2f(s[0][2] - m), __builtin_amdgcn_exp2f(s[0][3] - m)),
+        pack_bf16(__builtin_amdgcn_exp2f(s[1][0] - m), __builtin_amdgcn_exp2f(s[1][1] - m)),
+        pack_bf16(__builtin_amdgcn_exp2f(s[1][2] - m), __builtin_amdgcn_exp2f(s[1][3] - m))};
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      short4_t part[2];
+#pragma unroll
+      for (int rd = 0; rd < 2; ++rd)
+        part[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (short4_t __attribute__((address_space(3)))*)(vmine + vr_off[dt][rd]));
+      const u32x4 va = __builtin_bit_cast(
+          u32x4, short8_t{part[0][0], part[0][1], part[0][2], part[0][3], part[1][0], part[1][1],
+                          part[1][2], part[1][3]});
+      oacc[dt] = mfma16(va, pb, oacc[dt]);
+    }
+    lacc = mfma16(ones, pb, lacc);
+  };
+
+  Chunk buf[DEPTH];
+#pragma unroll
+  for (int it = 0; it < DEPTH; ++it) load_chunk(it, buf[it]);
+#pragma unroll
+  for (int it = 0; it < NCH; ++it) {
+    Chunk cur = buf[it % DEPTH];
+    if (it + DEPTH < NCH) load_chunk(it + DEPTH, buf[it % DEPTH]);
+    compute_chunk(it, cur);
+  }
+
+  // APPEND: wave 0 of the sequence's last split folds in the new token
+  // (position ctx - 1) from k_new / v_new, and writes it to its slot.
+  if constexpr (APPEND) {
+    if (split == nsplit - 1 && w == 0) {
+      store_new();
+      const uint16_t* kn = a.k_new + ((int64_t)seq * a.Hkv + kvh) * D;
+      const uint16_t* vn = a.v_new + ((int64_t)seq * a.Hkv + kvh) * D;
+      float d = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 kx = *(const u32x4*)(kn + 32 * ks + 8 * g);
+        d = dot2_bf16(qb[ks].x, kx.x, d);
+        d = dot2_bf16(qb[ks].y, kx.y, d);
+        d = dot2_bf16(qb[ks].z, kx.z, d);
+        d = dot2_bf16(qb[ks].w, kx.w, d);
+      }
+      d += shfl_xor(d, 16);
+      d += shfl_xor(d, 32);
+      const float sn = mul_rn(d, a.scale_log2e);
+      const float mnew = fmaxf(m, sn);
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      const float p = __builtin_amdgcn_exp2f(sn - mnew);
+      m = mnew;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const u32x2 vx = *(const u32x2*)(vn + 16 * dt + 4 * g);
+        const float vf[4] = {bf16lo(vx.x), bf16hi(vx.x), bf16lo(vx.y), bf16hi(vx.y)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) oacc[dt][e] = fmaf(p, vf[e], oacc[dt][e] * alpha);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) lacc[e] = fmaf(lacc[e], alpha, p);
+    }
+  }
+
+  // Merge the four waves: (m, l) per head in s_m / s_l, unnormalised O^T in the
+  // V areas (reused: [wave][head][dim] floats).
+  __syncthreads();  // every wave is done with its V area
+  float* s_o = (float*)s_v;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s_o[(w * kQR + qr) * D + 16 * dt + 4 * g + e] = oacc[dt][e];
+  }
+  if (g == 0) {
+    s_m[w][qr] = m;
+    s_l[w][qr] = lacc[0];
+  }
+  __syncthreads();
+
+  const int64_t unit = (int64_t)seq * a.hg + hg;
+  for (int i = tid; i < gh * D; i += blockDim.x) {
+    const int h = i / D;
+    const int dd = i - h * D;
+    float M = s_m[0][h];
+#pragma unroll
+    for (int ww = 1; ww < kW; ++ww) M = fmaxf(M, s_m[ww][h]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kW; ++ww) {
+      const float f = __builtin_amdgcn_exp2f(s_m[ww][h] - M);
+      L += s_l[ww][h] * f;
+      O += s_o[(ww * kQR + h) * D + dd] * f;
+    }
+    if (nsplit == 1) {
+      const int64_t o = ((int64_t)seq * a.Hq + h0 + h) * D + dd;
+      const float val = L > 0.f ? O / L : 0.f;
+      if (a.out_f32) ((float*)a.out)[o] = val;
+      else ((uint16_t*)a.out)[o] = (uint16_t)f32_to_bf16_rne(val);
+    } else {
+      const int64_t p = (unit * a.nsplit_max + split) * gt + h;
+      a.ws_o[p * D + dd] = O;
+      if (dd == 0) {
+        a.ws_ml[2 * p] = M;
+        a.ws_ml[2 * p + 1] = L;
+      }
+    }
+  }
+}
+
+// Production tiling: 2 chunks of 32 keys per wave (a split is 256 tokens),
+// both in flight.
+constexpr int kNch = 2;
+constexpr int kDepth = 2;
+
+template <int D, bool APPEND>
+int launch_mfma_d(const DecodeArgs& a, int B, hipStream_t stream) {
+  const unsigned nwg = (unsigned)((int64_t)B * a.hg * a.nsplit_max);
+  constexpr int S = kW * kNch * kCK;
+  if ((1 << a.bs_log2) >= S)
+    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, kNch, kDepth, APPEND, true>), dim3(nwg),
+                       dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, kNch, kDepth, APPEND, false>), dim3(nwg),
+                       dim3(256), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return -1;
+  const int gt = (a.group + a.nsub - 1) / a.nsub;
+  return a.nsplit_max > 1 ? launch_decode_combine(a, B, D, gt, stream) : 0;
+}
+
+}  // namespace
+
+
+int launch_paged_decode_mfma(const DecodeArgs& a, int B, int head_dim, bool append,
+                             hipStream_t stream) {
+  if (head_dim == 128) return append ? launch_mfma_d<128, true>(a, B, stream)
+                                     : launch_mfma_d<128, false>(a, B, stream);
+  if (head_dim == 64) return append ? launch_mfma_d<64, true>(a, B, stream)
+                                    : launch_mfma_d<64, false>(a, B, stream);
+  return -2;
+}
+
+}  // namespace pa

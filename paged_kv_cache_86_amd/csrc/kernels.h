@@ -20,6 +20,11 @@ constexpr int kLongSplitMinShort = 8;
 // ... and the grid with half the slots per sequence still has this many
 // workgroups (32 per compute unit of a 256-CU device).
 constexpr int64_t kLongSplitMinGrid = 8192;
+// Query heads per KV head from which bf16 decode runs on MFMA, the most heads
+// one MFMA workgroup serves, and its split length.
+constexpr int kMfmaMinGroup = 4;
+constexpr int kMfmaMaxGt = 16;
+constexpr int kMfmaSplitTokens = 256;
 
 int launch_kvcache_store(const void* k, const void* v, const int32_t* slot_mapping, int T,
                          void* k_cache, void* v_cache, int num_blocks, int block_size,
@@ -39,6 +44,7 @@ struct DecodePlan {
   int nsplit_short;  // short splits of the longest possible context
   bool long_splits;  // contexts above nsplit_max short splits use splits of twice the length
   int nsplit_max;    // workgroups (and partial slots) per (sequence, head group)
+  bool mfma;         // the MFMA kernel (bf16 pools, large query-head groups)
   int64_t units;   // (sequence, head group) pairs
   size_t ml_bytes, o_bytes;  // workspace regions: (max, sum) pairs, then unnormalised outputs
   size_t workspace_bytes() const { return ml_bytes + o_bytes; }
@@ -71,7 +77,12 @@ struct DecodeArgs {
 };
 
 int launch_paged_decode(const DecodeArgs& args, int B, int head_dim, int gt, bool kv8,
-                        bool append, hipStream_t stream);
+                        bool append, bool mfma, hipStream_t stream);
+int launch_paged_decode_mfma(const DecodeArgs& args, int B, int head_dim, bool append,
+                             hipStream_t stream);
+// Merge kernel of both decode kernels: split partials -> outputs.
+int launch_decode_combine(const DecodeArgs& args, int B, int head_dim, int gt,
+                          hipStream_t stream);
 
 int launch_kvcache_store_fp8(const void* k, const void* v, const int32_t* slot_mapping, int T,
                              void* k_cache, void* v_cache, int num_blocks, int block_size,

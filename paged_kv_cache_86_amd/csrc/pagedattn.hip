@@ -152,7 +152,7 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
     a.qscale_k = k_scale;
     a.qscale_v = v_scale;
   }
-  return pa::launch_paged_decode(a, num_seqs, head_dim, p.gt, kv8, append != nullptr,
+  return pa::launch_paged_decode(a, num_seqs, head_dim, p.gt, kv8, append != nullptr, p.mfma,
                                  (hipStream_t)stream) == 0
              ? PA_OK
              : PA_ERR_HIP;

@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-mixed", action="store_true")
+    ap.add_argument("--no-other", action="store_true", help="skip the 7B-shaped and "
+                    "max-concurrency decode legs")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--copy-probe", action="store_true",
@@ -272,6 +274,48 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": alg},
     }
+
+    # ---------------------------------------------------------------- other decode shapes
+    if not args.no_other:
+        result["other_decode"] = {}
+        # freed again below: the 7B-shaped pools are 2.7 GB
+        for cid, label in ((3, "7b-shaped decode, small pages: batch 256, 28 q / 4 kv heads, "
+                               "head_dim 128, block 16, ctx U[512,8192]"),
+                           (4, "max-concurrency decode: batch 512, 16 q / 8 kv heads, head_dim "
+                               "128, block 256, ctx log-normal (median 600) clipped to [1,4096], "
+                               "shared prefix blocks")):
+            o = config(cid)
+            okc, ovc = bf16(o.k_cache), bf16(o.v_cache)
+            oq, okn, ovn = bf16(o.q), bf16(o.k_new), bf16(o.v_new)
+            osl, obt, octx = i32(o.slot_mapping), i32(o.block_tables), i32(o.context_lens)
+            oout = torch.empty((o.batch, o.num_q_heads, o.head_dim), dtype=torch.bfloat16,
+                               device=dev)
+            ows = torch.empty(pa.decode_workspace_bytes(o.batch, o.num_q_heads, o.num_kv_heads,
+                                                        o.head_dim, o.block_size,
+                                                        o.max_blocks_per_seq),
+                              dtype=torch.uint8, device=dev)
+
+            def oappend():
+                pa.paged_decode_append(oq, okn, ovn, osl, okc, ovc, obt, octx, o.scale, oout,
+                                       workspace=ows)
+
+            ostep, _, oev, _ = timed_loop(torch, nothing, oappend, max(10, args.steps // 2),
+                                          max(3, args.warmup // 2), flush)
+            okv = o.kv_bytes()
+            ukv = o.unique_kv_bytes()  # blocks shared by several sequences counted once
+            oalg = decode_algorithmic_bytes(o) + store_bytes(o)
+            result["other_decode"][f"workload_{cid}"] = {
+                "workload": label,
+                "ms_per_step": round(ostep, 5),
+                "ms_per_step_events_median": round(float(np.median(oev)), 5),
+                "kv_gb_s": round(okv / (ostep * 1e-3) / 1e9, 2),
+                "pct_hbm_peak": round(100 * okv / (ostep * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                "achieved_gb_s": round(oalg / (ostep * 1e-3) / 1e9, 2),
+                "unique_kv_gb_s": round(ukv / (ostep * 1e-3) / 1e9, 2),
+                "tokens_per_s": round(o.batch / (ostep * 1e-3), 1),
+                "kernel": "MFMA decode" if o.num_q_heads // o.num_kv_heads >= 4 else "VALU decode"}
+            del okc, ovc, oq, okn, ovn, osl, obt, octx, oout, ows, o
+            torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- graph replay (extra leg)
     if not args.no_graph:

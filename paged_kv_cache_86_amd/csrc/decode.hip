@@ -569,8 +569,16 @@ __global__ __launch_bounds__(256) void paged_decode_combine_kernel(DecodeArgs a)
 #pragma unroll
     for (int sp = 0; sp < kCombineChunk; ++sp)
       if (sp < nsplit) O += pre[k][sp] * s_w[sp][h];
-    for (int sp = kCombineChunk; sp < nsplit; ++sp)
-      O += a.ws_o[(p0 + (int64_t)sp * GT + h) * D + d] * s_w[sp][h];
+    // Longer contexts: further splits in batches whose loads are issued together.
+    for (int base = kCombineChunk; base < nsplit; base += kCombineChunk) {
+      float t[kCombineChunk];
+#pragma unroll
+      for (int sp = 0; sp < kCombineChunk; ++sp)
+        t[sp] = a.ws_o[(p0 + (int64_t)min(base + sp, nsplit - 1) * GT + h) * D + d];
+#pragma unroll
+      for (int sp = 0; sp < kCombineChunk; ++sp)
+        if (base + sp < nsplit) O += t[sp] * s_w[base + sp][h];
+    }
     const int64_t o = ((int64_t)seq * a.Hq + h0 + h) * D + d;
     if (a.out_f32) ((float*)a.out)[o] = O;
     else ((uint16_t*)a.out)[o] = (uint16_t)f32_to_bf16_rne(O);

@@ -9,15 +9,16 @@
 // at HBM speed, so here both contractions of a split run on
 // v_mfma_f32_16x16x32_bf16 with the G heads as one 16-wide operand side:
 //
-//   * S^T = K Q^T per 16-key tile: the K operand (16 keys x 32 dims) is loaded
-//     straight from the cache into registers, 16 bytes per lane; Q^T sits in
-//     registers for the whole split (heads past G are zero);
+//   * S^T = K Q^T per 16-key tile; Q^T sits in registers for the whole split
+//     (heads past G are zero);
 //   * the softmax is per lane: lane l holds query head l % 16 and four keys of
 //     each tile, and the row max takes two exchanges;
-//   * O^T = V^T P^T: P^T comes from the S^T registers (bf16), the V^T operand
-//     needs V transposed, so each wave writes its V rows into a private LDS
-//     area (16-byte chunks XOR-swizzled by row) and reads them back with
-//     ds_read_b64_tr_b16; the 32 keys of a chunk map to the MFMA's 32
+//   * O^T = V^T P^T: P^T comes from the S^T registers (bf16);
+//   * K and V rows are loaded from the cache as whole 256-byte rows (four
+//     rows per 64-lane load, the fully coalesced pattern), then pass through a
+//     per-wave LDS area (16-byte chunks XOR-swizzled by row): K comes back in
+//     the MFMA operand layout (ds_read_b128), V transposed
+//     (ds_read_b64_tr_b16); the 32 keys of a chunk map to the MFMA's 32
 //     contraction slots in the same (permuted) order on both operands;
 //   * the softmax denominator is a third MFMA of P^T against ones, so it sums
 //     exactly the bf16 weights the PV product uses.
@@ -63,23 +64,27 @@ __device__ __forceinline__ int vswz(int r) {
 
 // One workgroup = one (sequence, head sub-group, split of S = kW * NCH * kCK
 // tokens); wave w takes chunks w, w + 4, ...  DEPTH chunks of K and V are in
-// flight per wave.
+// flight per wave.  Three waves per SIMD (at most 168 registers per lane).
 template <int D, int NCH, int DEPTH, bool APPEND, bool SCALAR_BLK>
-__global__ __launch_bounds__(256) void paged_decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+void paged_decode_mfma_kernel(DecodeArgs a) {
   constexpr int KS = D / 32;           // 32-dim contraction steps of S^T
   constexpr int DT = D / 16;           // 16-dim tiles of O^T
   constexpr int LPR = D / 8;           // lanes per V row (16-byte chunks)
   constexpr int RPI = 64 / LPR;        // V rows per 64-lane load
-  constexpr int NVL = kCK / RPI;       // V loads per lane per chunk
+  constexpr int NVL = kCK / RPI;       // K (and V) row loads per lane per chunk
   constexpr int S = kW * NCH * kCK;    // tokens per split
   constexpr int VROW = D * 2;          // bytes of a staged V row
   constexpr int VAREA = kCK * VROW;    // bytes of one wave's V area
   constexpr int NLB = D / 8;           // 16-byte vectors of a new K (or V) row
   static_assert(DEPTH >= 1 && DEPTH <= NCH, "prefetch depth");
-  static_assert(kW * VAREA >= kW * kQR * D * 4, "the V areas hold the merge");
+  constexpr int OROW = D + 4;          // floats per head row of the merge area (padded:
+                                       // the 16 heads of a write land on distinct banks)
+  constexpr int LDS_V = kW * VAREA;
+  constexpr int LDS_O = kW * kQR * OROW * 4;
 
-  // V staging during the loop; the per-wave (m, l, O) for the merge afterwards.
-  __shared__ __align__(16) char s_v[kW * VAREA];
+  // V staging during the loop; the per-wave unnormalised O for the merge afterwards.
+  __shared__ __align__(16) char s_v[LDS_V > LDS_O ? LDS_V : LDS_O];
   __shared__ int s_blk[SCALAR_BLK ? 1 : kMaxSplitIds];
   __shared__ float s_m[kW][kQR];
   __shared__ float s_l[kW][kQR];
@@ -104,7 +109,7 @@ __global__ __launch_bounds__(256) void paged_decode_mfma_kernel(DecodeArgs a) {
   const int b0 = t0 >> a.bs_log2;
   const int32_t* trow = a.block_tables + (int64_t)seq * a.mbs;
 
-  // Issued before the context length is known: block ids, q, the new token.
+  // Issued before the context length is known: block ids and q.
   int blk0 = -1;
   if constexpr (SCALAR_BLK) {
     const int b = b0 < a.mbs ? trow[b0] : -1;
@@ -128,27 +133,25 @@ __global__ __launch_bounds__(256) void paged_decode_mfma_kernel(DecodeArgs a) {
     const u32x4 v = *(const u32x4*)(qhead + 32 * ks + 8 * g);
     qb[ks] = qr < gh ? v : u32x4{0u, 0u, 0u, 0u};
   }
-  const bool new_lane = APPEND && tid < 2 * NLB;
-  const bool new_is_v = tid >= NLB;
-  const int new_c = new_is_v ? tid - NLB : tid;
-  u32x4 xnew{};
-  int slot = -1;
-  if constexpr (APPEND) {
-    if (new_lane) {
-      const uint16_t* src = new_is_v ? a.v_new : a.k_new;
-      xnew = *(const u32x4*)(src + ((int64_t)seq * a.Hkv + kvh) * D + new_c * 8);
-      slot = a.slot_mapping[seq];
-    }
-  }
   int ctx = a.context_lens[seq];
   const int cap = a.mbs << a.bs_log2;
   ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
   const int nsplit = ctx == 0 ? 1 : (ctx + S - 1) / S;
 
+  // APPEND: threads 0 .. 2*NLB-1 copy one 16-byte vector of the new K (V) row of
+  // this KV head into the sequence's slot (head sub-group 0 only).  Loaded
+  // here, at the end of one workgroup per sequence, to keep registers free.
   auto store_new = [&]() {
-    if (new_lane && sub == 0 && slot >= 0 && (int64_t)slot < a.num_slots) {
-      const int64_t dst = ((int64_t)slot * a.Hkv + kvh) * D + new_c * 8;
-      *(u32x4*)((uint16_t*)(new_is_v ? a.v_cache_w : a.k_cache_w) + dst) = xnew;
+    const bool new_is_v = tid >= NLB;
+    const int new_c = new_is_v ? tid - NLB : tid;
+    if (tid < 2 * NLB && sub == 0) {
+      const int slot = a.slot_mapping[seq];
+      if (slot >= 0 && (int64_t)slot < a.num_slots) {
+        const uint16_t* src = new_is_v ? a.v_new : a.k_new;
+        const u32x4 x = *(const u32x4*)(src + ((int64_t)seq * a.Hkv + kvh) * D + new_c * 8);
+        const int64_t dst = ((int64_t)slot * a.Hkv + kvh) * D + new_c * 8;
+        *(u32x4*)((uint16_t*)(new_is_v ? a.v_cache_w : a.k_cache_w) + dst) = x;
+      }
     }
   };
   if (ctx == 0) {  // padded row: output zeros
@@ -186,43 +189,42 @@ __global__ __launch_bounds__(256) void paged_decode_mfma_kernel(DecodeArgs a) {
   };
 
   char* vmine = s_v + w * VAREA;
-  // LDS byte offsets of this lane's V row chunk writes, and of its transposing
-  // reads: read rd of tile dt returns column 16 dt + qr at keys 16 rd + 4 g .. + 3.
+  // LDS byte offsets of this lane's row chunk writes (K, then V, of a chunk),
+  // of its K operand reads (row 16 kt + qr, chunk 4 ks + g; the swizzle does
+  // not depend on kt), and of its transposing V reads: read rd of tile dt
+  // returns column 16 dt + qr at keys 16 rd + 4 g .. + 3.
   int vw_off[NVL];
 #pragma unroll
   for (int i = 0; i < NVL; ++i) {
     const int r = i * RPI + lane / LPR;
     vw_off[i] = r * VROW + (((lane % LPR) ^ vswz<D>(r)) * 16);
   }
-  int vr_off[DT][2];
+  int kr_off[KS];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
+  for (int ks = 0; ks < KS; ++ks) kr_off[ks] = qr * VROW + (((4 * ks + g) ^ vswz<D>(qr)) * 16);
+  // The transposing read of (dt, rd) starts at element 16 dt + 4 (qr & 3) of row r:
+  // chunk 2 dt + ((qr & 3) >> 1), element (qr & 1) * 4; with the swizzle that is
+  // vr_base[rd] + ((2 dt ^ vr_swz[rd]) << 4) (2 dt has no bit 0).
+  int vr_base[2], vr_swz[2];
 #pragma unroll
-    for (int rd = 0; rd < 2; ++rd) {
-      const int r = 16 * rd + 4 * g + (qr >> 2);
-      const int dcol = 16 * dt + 4 * (qr & 3);
-      vr_off[dt][rd] = r * VROW + (((dcol >> 3) ^ vswz<D>(r)) * 16) + (dcol & 7) * 2;
-    }
+  for (int rd = 0; rd < 2; ++rd) {
+    const int r = 16 * rd + 4 * g + (qr >> 2);
+    const int sw = vswz<D>(r);
+    vr_base[rd] = r * VROW + ((((qr & 3) >> 1) ^ (sw & 1)) << 4) + (qr & 1) * 8;
+    vr_swz[rd] = sw & ~1;
   }
 
   struct Chunk {
-    u32x4 k[2][KS];  // K operand: keys 16 kt + qr, dims 32 ks + 8 g .. + 7
-    u32x4 v[NVL];    // V rows i * RPI + lane / LPR, chunk lane % LPR
+    u32x4 k[NVL];  // K rows i * RPI + lane / LPR, chunk lane % LPR
+    u32x4 v[NVL];  // V rows, the same
   };
   auto load_chunk = [&](int it, Chunk& ch) {
     const int k0 = t0 + (it * kW + w) * kCK;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int j = k0 + 16 * kt + qr;
-      const int64_t row = j < t1 ? row_of(j) : -1;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        ch.k[kt][ks] = __builtin_nontemporal_load(kv_ptr(a.k_cache, row, 32 * ks + 8 * g));
-    }
-#pragma unroll
     for (int i = 0; i < NVL; ++i) {
       const int j = k0 + i * RPI + lane / LPR;
       const int64_t row = j < t1 ? row_of(j) : -1;
+      ch.k[i] = __builtin_nontemporal_load(kv_ptr(a.k_cache, row, (lane % LPR) * 8));
       ch.v[i] = __builtin_nontemporal_load(kv_ptr(a.v_cache, row, (lane % LPR) * 8));
     }
   };
@@ -236,14 +238,20 @@ __global__ __launch_bounds__(256) void paged_decode_mfma_kernel(DecodeArgs a) {
 
   auto compute_chunk = [&](int it, const Chunk& ch) {
     const int k0 = t0 + (it * kW + w) * kCK;
+    // K rows through this wave's LDS area into the operand layout, then V rows
+    // (read back transposed below; the wave's LDS accesses stay in order).
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) *(u32x4*)(vmine + vw_off[i]) = ch.k[i];
     f32x4_t sacc[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       sacc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) sacc[kt] = mfma16(ch.k[kt][ks], qb[ks], sacc[kt]);
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 ka = *(const u32x4*)(vmine + kr_off[ks] + kt * 16 * VROW);
+        sacc[kt] = mfma16(ka, qb[ks], sacc[kt]);
+      }
     }
-    // V rows into this wave's LDS area (read back transposed below).
 #pragma unroll
     for (int i = 0; i < NVL; ++i) *(u32x4*)(vmine + vw_off[i]) = ch.v[i];
     // Scores of keys k0 + 16 kt + 4 g + e (log2 units), masked to -inf.
@@ -284,7 +292,8 @@ __global__ __launch_bounds__(256) void paged_decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int rd = 0; rd < 2; ++rd)
         part[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (short4_t __attribute__((address_space(3)))*)(vmine + vr_off[dt][rd]));
+            (short4_t __attribute__((address_space(3)))*)(vmine + vr_base[rd] +
+                                                           (((2 * dt) ^ vr_swz[rd]) << 4)));
       const u32x4 va = __builtin_bit_cast(
           u32x4, short8_t{part[0][0], part[0][1], part[0][2], part[0][3], part[1][0], part[1][1],
                           part[1][2], part[1][3]});
@@ -339,13 +348,13 @@ __global__ __launch_bounds__(256) void paged_decode_mfma_kernel(DecodeArgs a) {
   }
 
   // Merge the four waves: (m, l) per head in s_m / s_l, unnormalised O^T in the
-  // V areas (reused: [wave][head][dim] floats).
+  // V areas (reused: [wave][head][dim] floats, rows padded).
   __syncthreads();  // every wave is done with its V area
   float* s_o = (float*)s_v;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) s_o[(w * kQR + qr) * D + 16 * dt + 4 * g + e] = oacc[dt][e];
+    for (int e = 0; e < 4; ++e) s_o[(w * kQR + qr) * OROW + 16 * dt + 4 * g + e] = oacc[dt][e];
   }
   if (g == 0) {
     s_m[w][qr] = m;
@@ -365,7 +374,7 @@ __global__ __launch_bounds__(256) void paged_decode_mfma_kernel(DecodeArgs a) {
     for (int ww = 0; ww < kW; ++ww) {
       const float f = __builtin_amdgcn_exp2f(s_m[ww][h] - M);
       L += s_l[ww][h] * f;
-      O += s_o[(ww * kQR + h) * D + dd] * f;
+      O += s_o[(ww * kQR + h) * OROW + dd] * f;
     }
     if (nsplit == 1) {
       const int64_t o = ((int64_t)seq * a.Hq + h0 + h) * D + dd;

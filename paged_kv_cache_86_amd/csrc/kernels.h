@@ -22,7 +22,7 @@ constexpr int kLongSplitMinShort = 8;
 constexpr int64_t kLongSplitMinGrid = 8192;
 // Query heads per KV head from which bf16 decode runs on MFMA, the most heads
 // one MFMA workgroup serves, and its split length.
-constexpr int kMfmaMinGroup = 4;
+constexpr int kMfmaMinGroup = 3;
 constexpr int kMfmaMaxGt = 16;
 constexpr int kMfmaSplitTokens = 256;
 

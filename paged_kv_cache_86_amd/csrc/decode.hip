@@ -694,9 +694,10 @@ int launch_decode_combine(const DecodeArgs& a, int B, int head_dim, int gt, hipS
 DecodePlan plan_decode(int B, int Hq, int Hkv, int head_dim, int block_size, int mbs, bool kv8) {
   DecodePlan p{};
   p.group = Hq / Hkv;
-  // Groups of kMfmaMinGroup or more query heads per KV head run the MFMA
-  // kernel (bf16 pools): the VALU kernel's vector work grows with the group.
-  p.mfma = !kv8 && p.group >= kMfmaMinGroup;
+  // Groups of kMfmaMinGroup (FP8 pools: kMfmaMinGroupFp8) or more query heads
+  // per KV head run the MFMA kernel: the VALU kernel's vector work grows with
+  // the group.
+  p.mfma = p.group >= (kv8 ? kMfmaMinGroupFp8 : kMfmaMinGroup);
   const int gmax = p.mfma ? kMfmaMaxGt : (kv8 ? max_gt<true>() : max_gt<false>());
   p.nsub = (p.group + gmax - 1) / gmax;
   p.gt = (p.group + p.nsub - 1) / p.nsub;
@@ -730,7 +731,7 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int head_dim, int block_size, int
 int launch_paged_decode(const DecodeArgs& a, int B, int head_dim, int gt, bool kv8, bool append,
                         bool mfma, hipStream_t stream) {
   if (B == 0) return 0;
-  if (mfma) return kv8 ? -2 : launch_paged_decode_mfma(a, B, head_dim, append, stream);
+  if (mfma) return launch_paged_decode_mfma(a, B, head_dim, kv8, append, stream);
   if (kv8) {
     return append ? launch_head_dim<true, true>(a, B, head_dim, gt, stream)
                   : launch_head_dim<true, false>(a, B, head_dim, gt, stream);

@@ -25,7 +25,14 @@
 //
 // Masked keys (past the split's last cached token, or in a block the table
 // does not map) get score -inf and read the query head's row instead of the
-// cache, so that p = 0 multiplies finite values.
+// cache (zeroed for KV8), so that p = 0 multiplies finite values.
+//
+// KV8 reads an FP8 (OCP E4M3) cache: a row of one head is D codes, a 16-byte
+// load carries 16 of them, and they are widened exactly to bf16 (scale 1) on
+// their way into the LDS area, so the MFMA part is unchanged; the per-tensor
+// K scale is folded into the score scale and the V scale multiplies the merged
+// outputs.  The fused store quantizes the new row exactly as the store kernel
+// does, and the new token is attended with the values its codes decode to.
 #include "common.h"
 #include "kernels.h"
 
@@ -65,14 +72,16 @@ __device__ __forceinline__ int vswz(int r) {
 // One workgroup = one (sequence, head sub-group, split of S = kW * NCH * kCK
 // tokens); wave w takes chunks w, w + 4, ...  DEPTH chunks of K and V are in
 // flight per wave.  Three waves per SIMD (at most 168 registers per lane).
-template <int D, int NCH, int DEPTH, bool APPEND, bool SCALAR_BLK>
+template <int D, int NCH, int DEPTH, bool KV8, bool APPEND, bool SCALAR_BLK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 void paged_decode_mfma_kernel(DecodeArgs a) {
   constexpr int KS = D / 32;           // 32-dim contraction steps of S^T
   constexpr int DT = D / 16;           // 16-dim tiles of O^T
-  constexpr int LPR = D / 8;           // lanes per V row (16-byte chunks)
-  constexpr int RPI = 64 / LPR;        // V rows per 64-lane load
+  constexpr int EPL = KV8 ? 16 : 8;    // cache elements per 16-byte load
+  constexpr int LPR = D / EPL;         // lanes per cache row of one head
+  constexpr int RPI = 64 / LPR;        // rows per 64-lane load
   constexpr int NVL = kCK / RPI;       // K (and V) row loads per lane per chunk
+  constexpr int EB = KV8 ? 1 : 2;      // bytes per cache element
   constexpr int S = kW * NCH * kCK;    // tokens per split
   constexpr int VROW = D * 2;          // bytes of a staged V row
   constexpr int VAREA = kCK * VROW;    // bytes of one wave's V area
@@ -149,8 +158,12 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
       if (slot >= 0 && (int64_t)slot < a.num_slots) {
         const uint16_t* src = new_is_v ? a.v_new : a.k_new;
         const u32x4 x = *(const u32x4*)(src + ((int64_t)seq * a.Hkv + kvh) * D + new_c * 8);
-        const int64_t dst = ((int64_t)slot * a.Hkv + kvh) * D + new_c * 8;
-        *(u32x4*)((uint16_t*)(new_is_v ? a.v_cache_w : a.k_cache_w) + dst) = x;
+        const int64_t dst = ((int64_t)slot * a.Hkv + kvh) * D + new_c * 8;  // element index
+        if constexpr (KV8)
+          *(u32x2*)((char*)(new_is_v ? a.v_cache_w : a.k_cache_w) + dst) =
+              quantize8(x, new_is_v ? a.qscale_v : a.qscale_k);
+        else
+          *(u32x4*)((uint16_t*)(new_is_v ? a.v_cache_w : a.k_cache_w) + dst) = x;
       }
     }
   };
@@ -183,9 +196,11 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
     if (blk < 0) return -1;
     return (((int64_t)blk << a.bs_log2) + (j & bs_mask)) * row_stride + (int64_t)kvh * D;
   };
-  // Unmapped rows are read from the query head instead (finite; masked out).
+  // Unmapped rows are read from the query head instead (finite, also as FP8
+  // codes; masked out).
   auto kv_ptr = [&](const uint16_t* base, int64_t row, int elem) -> const u32x4* {
-    return (const u32x4*)(row >= 0 ? base + row + elem : qhead + elem);
+    return row >= 0 ? (const u32x4*)((const char*)base + (row + elem) * EB)
+                    : (const u32x4*)((const char*)qhead + elem * EB);
   };
 
   char* vmine = s_v + w * VAREA;
@@ -193,12 +208,39 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
   // of its K operand reads (row 16 kt + qr, chunk 4 ks + g; the swizzle does
   // not depend on kt), and of its transposing V reads: read rd of tile dt
   // returns column 16 dt + qr at keys 16 rd + 4 g .. + 3.
-  int vw_off[NVL];
+  // (KV8: a load's 16 codes become two 16-byte bf16 chunks, 2c and 2c + 1.)
+  constexpr int CPL = KV8 ? 2 : 1;
+  int vw_off[NVL][CPL];
 #pragma unroll
   for (int i = 0; i < NVL; ++i) {
     const int r = i * RPI + lane / LPR;
-    vw_off[i] = r * VROW + (((lane % LPR) ^ vswz<D>(r)) * 16);
+#pragma unroll
+    for (int h = 0; h < CPL; ++h)
+      vw_off[i][h] = r * VROW + ((((lane % LPR) * CPL + h) ^ vswz<D>(r)) * 16);
   }
+  // Row chunks of a load into the wave's LDS area (widened for KV8; rows that
+  // came from the query head instead of the cache are zeroed, since its bytes
+  // read as E4M3 codes may be NaN).
+  auto put_rows = [&](const u32x4 (&rows)[NVL], uint32_t ok) {
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) {
+      if constexpr (KV8) {
+        const bool oki = (ok >> i) & 1u;
+        const uint32_t cw[4] = {oki ? rows[i].x : 0u, oki ? rows[i].y : 0u, oki ? rows[i].z : 0u,
+                                oki ? rows[i].w : 0u};
+        uint32_t b[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          b[2 * e] = fp8x2_to_bf16x2<false>(cw[e]);
+          b[2 * e + 1] = fp8x2_to_bf16x2<true>(cw[e]);
+        }
+        *(u32x4*)(vmine + vw_off[i][0]) = u32x4{b[0], b[1], b[2], b[3]};
+        *(u32x4*)(vmine + vw_off[i][1]) = u32x4{b[4], b[5], b[6], b[7]};
+      } else {
+        *(u32x4*)(vmine + vw_off[i][0]) = rows[i];
+      }
+    }
+  };
   int kr_off[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) kr_off[ks] = qr * VROW + (((4 * ks + g) ^ vswz<D>(qr)) * 16);
@@ -217,15 +259,18 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
   struct Chunk {
     u32x4 k[NVL];  // K rows i * RPI + lane / LPR, chunk lane % LPR
     u32x4 v[NVL];  // V rows, the same
+    uint32_t ok;   // bit i: row i came from the cache (KV8 only)
   };
   auto load_chunk = [&](int it, Chunk& ch) {
     const int k0 = t0 + (it * kW + w) * kCK;
+    ch.ok = 0;
 #pragma unroll
     for (int i = 0; i < NVL; ++i) {
       const int j = k0 + i * RPI + lane / LPR;
       const int64_t row = j < t1 ? row_of(j) : -1;
-      ch.k[i] = __builtin_nontemporal_load(kv_ptr(a.k_cache, row, (lane % LPR) * 8));
-      ch.v[i] = __builtin_nontemporal_load(kv_ptr(a.v_cache, row, (lane % LPR) * 8));
+      if constexpr (KV8) ch.ok |= (row >= 0 ? 1u : 0u) << i;
+      ch.k[i] = __builtin_nontemporal_load(kv_ptr(a.k_cache, row, (lane % LPR) * EPL));
+      ch.v[i] = __builtin_nontemporal_load(kv_ptr(a.v_cache, row, (lane % LPR) * EPL));
     }
   };
 
@@ -240,8 +285,7 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
     const int k0 = t0 + (it * kW + w) * kCK;
     // K rows through this wave's LDS area into the operand layout, then V rows
     // (read back transposed below; the wave's LDS accesses stay in order).
-#pragma unroll
-    for (int i = 0; i < NVL; ++i) *(u32x4*)(vmine + vw_off[i]) = ch.k[i];
+    put_rows(ch.k, ch.ok);
     f32x4_t sacc[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -252,8 +296,7 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
         sacc[kt] = mfma16(ka, qb[ks], sacc[kt]);
       }
     }
-#pragma unroll
-    for (int i = 0; i < NVL; ++i) *(u32x4*)(vmine + vw_off[i]) = ch.v[i];
+    put_rows(ch.v, ch.ok);
     // Scores of keys k0 + 16 kt + 4 g + e (log2 units), masked to -inf.
     float s[2][4];
     float mx = -INFINITY;
@@ -322,7 +365,12 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
       float d = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 kx = *(const u32x4*)(kn + 32 * ks + 8 * g);
+        u32x4 kx = *(const u32x4*)(kn + 32 * ks + 8 * g);
+        if constexpr (KV8) {  // the values its codes decode to (unscaled, exact in bf16)
+          const u32x2 cw = quantize8(kx, a.qscale_k);
+          kx = u32x4{fp8x2_to_bf16x2<false>(cw.x), fp8x2_to_bf16x2<true>(cw.x),
+                     fp8x2_to_bf16x2<false>(cw.y), fp8x2_to_bf16x2<true>(cw.y)};
+        }
         d = dot2_bf16(qb[ks].x, kx.x, d);
         d = dot2_bf16(qb[ks].y, kx.y, d);
         d = dot2_bf16(qb[ks].z, kx.z, d);
@@ -338,7 +386,16 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const u32x2 vx = *(const u32x2*)(vn + 16 * dt + 4 * g);
-        const float vf[4] = {bf16lo(vx.x), bf16hi(vx.x), bf16lo(vx.y), bf16hi(vx.y)};
+        float vf[4] = {bf16lo(vx.x), bf16hi(vx.x), bf16lo(vx.y), bf16hi(vx.y)};
+        if constexpr (KV8) {
+          const uint32_t c2 = fp8_code_pair(vf[0], vf[1], a.qscale_v) |
+                              (fp8_code_pair(vf[2], vf[3], a.qscale_v) << 16);
+          const float2_t lo = fp8x2_to_f32x2<false>(c2), hi = fp8x2_to_f32x2<true>(c2);
+          vf[0] = lo.x;
+          vf[1] = lo.y;
+          vf[2] = hi.x;
+          vf[3] = hi.y;
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) oacc[dt][e] = fmaf(p, vf[e], oacc[dt][e] * alpha);
       }
@@ -376,6 +433,7 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
       L += s_l[ww][h] * f;
       O += s_o[(ww * kQR + h) * OROW + dd] * f;
     }
+    if constexpr (KV8) O *= a.v_scale;
     if (nsplit == 1) {
       const int64_t o = ((int64_t)seq * a.Hq + h0 + h) * D + dd;
       const float val = L > 0.f ? O / L : 0.f;
@@ -397,30 +455,35 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
 constexpr int kNch = 2;
 constexpr int kDepth = 2;
 
-template <int D, bool APPEND>
+template <int D, bool KV8, bool APPEND>
 int launch_mfma_d(const DecodeArgs& a, int B, hipStream_t stream) {
   const unsigned nwg = (unsigned)((int64_t)B * a.hg * a.nsplit_max);
   constexpr int S = kW * kNch * kCK;
   if ((1 << a.bs_log2) >= S)
-    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, kNch, kDepth, APPEND, true>), dim3(nwg),
+    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, kNch, kDepth, KV8, APPEND, true>), dim3(nwg),
                        dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, kNch, kDepth, APPEND, false>), dim3(nwg),
+    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, kNch, kDepth, KV8, APPEND, false>), dim3(nwg),
                        dim3(256), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return -1;
   const int gt = (a.group + a.nsub - 1) / a.nsub;
   return a.nsplit_max > 1 ? launch_decode_combine(a, B, D, gt, stream) : 0;
 }
 
+template <int D>
+int launch_mfma_dd(const DecodeArgs& a, int B, bool kv8, bool append, hipStream_t stream) {
+  if (kv8) return append ? launch_mfma_d<D, true, true>(a, B, stream)
+                         : launch_mfma_d<D, true, false>(a, B, stream);
+  return append ? launch_mfma_d<D, false, true>(a, B, stream)
+                : launch_mfma_d<D, false, false>(a, B, stream);
+}
+
 }  // namespace
 
-
-int launch_paged_decode_mfma(const DecodeArgs& a, int B, int head_dim, bool append,
+int launch_paged_decode_mfma(const DecodeArgs& a, int B, int head_dim, bool kv8, bool append,
                              hipStream_t stream) {
-  if (head_dim == 128) return append ? launch_mfma_d<128, true>(a, B, stream)
-                                     : launch_mfma_d<128, false>(a, B, stream);
-  if (head_dim == 64) return append ? launch_mfma_d<64, true>(a, B, stream)
-                                    : launch_mfma_d<64, false>(a, B, stream);
+  if (head_dim == 128) return launch_mfma_dd<128>(a, B, kv8, append, stream);
+  if (head_dim == 64) return launch_mfma_dd<64>(a, B, kv8, append, stream);
   return -2;
 }
 

@@ -20,9 +20,10 @@ constexpr int kLongSplitMinShort = 8;
 // ... and the grid with half the slots per sequence still has this many
 // workgroups (32 per compute unit of a 256-CU device).
 constexpr int64_t kLongSplitMinGrid = 8192;
-// Query heads per KV head from which bf16 decode runs on MFMA, the most heads
-// one MFMA workgroup serves, and its split length.
+// Query heads per KV head from which decode runs on MFMA (bf16 and FP8
+// pools), the most heads one MFMA workgroup serves, and its split length.
 constexpr int kMfmaMinGroup = 3;
+constexpr int kMfmaMinGroupFp8 = 3;
 constexpr int kMfmaMaxGt = 16;
 constexpr int kMfmaSplitTokens = 256;
 
@@ -78,7 +79,7 @@ struct DecodeArgs {
 
 int launch_paged_decode(const DecodeArgs& args, int B, int head_dim, int gt, bool kv8,
                         bool append, bool mfma, hipStream_t stream);
-int launch_paged_decode_mfma(const DecodeArgs& args, int B, int head_dim, bool append,
+int launch_paged_decode_mfma(const DecodeArgs& args, int B, int head_dim, bool kv8, bool append,
                              hipStream_t stream);
 // Merge kernel of both decode kernels: split partials -> outputs.
 int launch_decode_combine(const DecodeArgs& args, int B, int head_dim, int gt,

@@ -167,11 +167,14 @@ def test_decode_fp8_workspace_sizes():
         pa.decode_workspace_bytes(64, 16, 8, 128, 256, 16)
     assert pa.decode_fp8_workspace_bytes(64, 64, 8, 128, 16, 64) == \
         pa.decode_workspace_bytes(64, 64, 8, 128, 16, 64)
-    # a group of 5: bf16 serves it as one workgroup of 5 heads, FP8 as two of 3
+    # a group of 5 runs the MFMA kernel (bf16 and FP8): one workgroup of 5 heads; a group of 2
+    # on FP8 runs the VALU kernel, and 20 heads per KV head the MFMA kernel as two of 10
     def ws(parts):  # (max, sum) pairs then 128-float outputs, each region rounded up to 256 B
         return -(-parts * 8 // 256) * 256 + -(-parts * 512 // 256) * 256
     assert pa.decode_workspace_bytes(1, 5, 1, 128, 256, 16) == ws(16 * 5)
-    assert pa.decode_fp8_workspace_bytes(1, 5, 1, 128, 256, 16) == ws(16 * 6)
+    assert pa.decode_fp8_workspace_bytes(1, 5, 1, 128, 256, 16) == ws(16 * 5)
+    assert pa.decode_fp8_workspace_bytes(1, 2, 1, 128, 256, 16) == ws(16 * 2)
+    assert pa.decode_fp8_workspace_bytes(1, 20, 1, 128, 256, 16) == ws(16 * 20)
     assert pa.decode_fp8_workspace_bytes(4, 6, 4, 128, 16, 8) == 0
 
 

@@ -106,8 +106,11 @@ SMALL = [
     (128, 16, 28, 4, [512, 1, 300, 8192 // 8]),
     (128, 256, 16, 8, [1, 255, 256, 257, 511, 512, 513, 4096]),
     (128, 32, 7, 1, [129, 33, 2000]),
-    (128, 16, 12, 1, [100, 1, 777]),           # 12 heads per KV head: two sub-groups of 6
-    (64, 64, 16, 1, [5, 300, 1024]),           # 16 heads per KV head: two sub-groups of 8
+    (128, 16, 12, 1, [100, 1, 777]),           # 12 heads per KV head (MFMA kernel)
+    (64, 64, 16, 1, [5, 300, 1024]),           # 16 heads per KV head: one MFMA workgroup
+    (128, 16, 20, 1, [700, 1, 257]),           # 20 heads: two MFMA sub-groups of 10
+    (64, 32, 32, 1, [64, 1000, 3]),            # 32 heads: two MFMA sub-groups of 16
+    (128, 64, 3, 1, [1, 64, 65, 1000]),        # 3 heads: the smallest MFMA group
     (128, 512, 3, 3, [1500, 2]),
     (128, 1024, 2, 2, [3000, 1025]),
 ]

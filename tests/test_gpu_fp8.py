@@ -156,11 +156,13 @@ SMALL = [
     (64, 16, 2, 1, [17, 64, 200, 255, 513]),
     (64, 1, 4, 4, [1, 2, 3, 70]),
     (64, 8, 8, 2, [0, 1, 7, 8, 9, 0, 63, 64, 65]),
-    (128, 16, 28, 4, [512, 1, 300, 1024]),          # 7 heads per KV head: sub-groups of 4 and 3
+    (128, 16, 28, 4, [512, 1, 300, 1024]),          # 7 heads per KV head (MFMA kernel)
     (128, 256, 16, 8, [1, 255, 256, 257, 511, 512, 513, 4096]),
-    (128, 32, 5, 1, [129, 33, 2000]),               # 5 heads: sub-groups of 3 and 2
-    (128, 16, 32, 4, [100, 1, 777]),                # 8 heads: two sub-groups of 4
-    (64, 64, 16, 1, [5, 300, 1024]),                # 16 heads: four sub-groups of 4
+    (128, 32, 5, 1, [129, 33, 2000]),               # 5 heads (MFMA)
+    (128, 16, 32, 4, [100, 1, 777]),                # 8 heads (MFMA)
+    (64, 64, 16, 1, [5, 300, 1024]),                # 16 heads: one MFMA workgroup
+    (128, 16, 20, 1, [700, 1, 257]),                # 20 heads: two MFMA sub-groups of 10
+    (64, 32, 32, 1, [64, 1000, 3]),                 # 32 heads: two MFMA sub-groups of 16
     (128, 1024, 2, 2, [3000, 1025]),
 ]
 

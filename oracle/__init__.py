@@ -19,6 +19,7 @@ from .fp8 import (  # noqa: F401
     e4m3_encode,
     kvcache_store_fp8,
     paged_decode_fp8,
+    paged_prefill_fp8,
     quantize,
 )
 from .paged_attention import (  # noqa: F401

@@ -20,7 +20,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .paged_attention import bf16_to_f64, kv_head_for, softmax_attention, unpage
+from .paged_attention import bf16_to_f64, kv_head_for, softmax_attention, unpage, visible
 
 E4M3_MAX = 448.0
 
@@ -109,4 +109,36 @@ def paged_decode_fp8(q, k_cache8, v_cache8, block_tables, context_lens, scale, k
             g = kv_head_for(h, group)
             qh = bf16_to_f64(q[i, h])[None, :]
             out[i, h] = softmax_attention(qh, K[:, g, :], V[:, g, :], scale)[0]
+    return out
+
+
+def paged_prefill_fp8(q, cu_seqlens_q, k_cache8, v_cache8, block_tables, context_lens, scale,
+                      k_scale, v_scale) -> np.ndarray:
+    """Prefix-hit prefill over an FP8 cache; ``[Tq, Hq, D]`` float64.
+
+    The chunk's own tokens are already in the cache (stored before attention, as
+    the store-then-attend order of a step has it), so every key ``0 .. ctx-1`` of
+    sequence ``i`` is read through its block table and dequantized; chunk token
+    ``t`` sits at position ``P + t`` with ``P = context_lens[i] - q_len_i`` and
+    sees keys ``0 .. P + t``.
+    """
+    Tq, Hq, D = q.shape
+    Hkv = k_cache8.shape[2]
+    group = Hq // Hkv
+    out = np.zeros((Tq, Hq, D), dtype=np.float64)
+    cu = np.asarray(cu_seqlens_q, dtype=np.int64)
+    for i in range(cu.shape[0] - 1):
+        a, b = int(cu[i]), int(cu[i + 1])
+        n = b - a
+        if n == 0:
+            continue
+        ctx = int(context_lens[i])
+        P = ctx - n
+        K = dequantize(unpage(k_cache8, block_tables[i], ctx), k_scale)
+        V = dequantize(unpage(v_cache8, block_tables[i], ctx), v_scale)
+        mask = visible(np.arange(n)[:, None], np.arange(ctx)[None, :], P)
+        for h in range(Hq):
+            g = kv_head_for(h, group)
+            Qh = bf16_to_f64(q[a:b, h])
+            out[a:b, h] = softmax_attention(Qh, K[:, g, :], V[:, g, :], scale, mask)
     return out

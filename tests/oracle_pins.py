@@ -420,6 +420,54 @@ def pin_fp8_decode_reduces_to_bf16_decode():
     assert np.max(np.abs(a2 - b2)) < 1e-12
 
 
+def _fp8_prefill_inputs(seed, prefix_lens, q_lens, k_scale, v_scale, Hq=4, Hkv=2, D=64, BS=16):
+    """A prefill chunk with FP8 pools holding the prefix and, stored, the chunk's own tokens."""
+    from oracle import kvcache_store_fp8, quantize
+    p = _prefill_inputs(seed, prefix_lens, q_lens, Hq=Hq, Hkv=Hkv, D=D, BS=BS)
+    kc8, vc8 = kvcache_store_fp8(p.k_new, p.v_new, p.slot_mapping, quantize(p.k_cache, k_scale),
+                                 quantize(p.v_cache, v_scale), k_scale, v_scale)
+    return p, kc8, vc8
+
+
+def pin_fp8_prefill_rows_equal_fp8_decode_steps():
+    """Chunk row t over an FP8 cache equals an FP8 decode of that token over P + t + 1 keys."""
+    from oracle import paged_decode_fp8, paged_prefill_fp8
+    ks, vs = 0.013, 0.021
+    p, kc8, vc8 = _fp8_prefill_inputs(35, [0, 13, 24], [6, 9, 1], ks, vs)
+    out = paged_prefill_fp8(p.q, p.cu_seqlens_q, kc8, vc8, p.block_tables, p.context_lens,
+                            SCALE64, ks, vs)
+    for i in range(p.batch):
+        for t in range(int(p.q_lens[i])):
+            row = int(p.cu_seqlens_q[i]) + t
+            ctx = np.array([int(p.prefix_lens[i]) + t + 1], np.int32)
+            dec = paged_decode_fp8(p.q[row:row + 1], kc8, vc8, p.block_tables[i:i + 1], ctx,
+                                   SCALE64, ks, vs)
+            assert np.max(np.abs(out[row] - dec[0])) < 1e-12, (i, t)
+
+
+def pin_fp8_prefill_reduces_to_bf16_prefill():
+    """Scales 1 and values exactly representable in E4M3: FP8 prefill equals the bf16 prefill
+    whose prefix and new K/V are those values (bit-exact: bf16 holds every E4M3 value)."""
+    from oracle import paged_prefill_fp8
+    p = _prefill_inputs(36, [5, 40], [7, 3], Hq=6, Hkv=2, D=64, BS=8)
+    rng = np.random.default_rng(37)
+    kc8 = rng.integers(0, 0x7F, size=p.k_cache.shape).astype(np.uint8) | (
+        rng.integers(0, 2, size=p.k_cache.shape).astype(np.uint8) << 7)
+    vc8 = rng.integers(0, 0x7F, size=p.v_cache.shape).astype(np.uint8)
+
+    def bits(codes):
+        return (oracle.e4m3_decode(codes).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    kb, vb = bits(kc8), bits(vc8)
+    slots = p.slot_mapping
+    k_new = np.stack([kb[s // 8, s % 8] for s in slots])
+    v_new = np.stack([vb[s // 8, s % 8] for s in slots])
+    a = paged_prefill_fp8(p.q, p.cu_seqlens_q, kc8, vc8, p.block_tables, p.context_lens, SCALE64,
+                          1.0, 1.0)
+    b = oracle.paged_prefill(p.q, k_new, v_new, p.cu_seqlens_q, kb, vb, p.block_tables,
+                             p.context_lens, SCALE64)
+    assert np.array_equal(a, b)
+
+
 def pin_fp8_store_writes_exactly_mapped_slots():
     from oracle import kvcache_store_fp8, quantize
     rng = np.random.default_rng(34)

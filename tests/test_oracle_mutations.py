@@ -98,6 +98,26 @@ def _encode_truncate(x):
     lo = np.clip(np.searchsorted(vals, np.minimum(a, 448.0), side="right") - 1, 0, 0x7E)
     return (lo.astype(np.uint8) | (np.signbit(x).astype(np.uint8) << 7)).astype(np.uint8)
 
+ORIGINAL_PREFILL_FP8 = fp8_oracle.paged_prefill_fp8
+
+
+def _prefill_fp8_swapped_scales(q, cu, kc8, vc8, bt, ctx, scale, k_scale, v_scale):
+    return ORIGINAL_PREFILL_FP8(q, cu, kc8, vc8, bt, ctx, scale, v_scale, k_scale)
+
+
+def _prefill_fp8_sees_whole_chunk(q, cu, kc8, vc8, bt, ctx, scale, k_scale, v_scale):
+    # every chunk token treated as the last one: no causal mask inside the chunk
+    out = np.zeros(q.shape, dtype=np.float64)
+    cu = np.asarray(cu, dtype=np.int64)
+    for i in range(cu.shape[0] - 1):
+        a, b = int(cu[i]), int(cu[i + 1])
+        for t in range(a, b):
+            out[t] = oracle.paged_decode_fp8(q[t:t + 1], kc8, vc8, bt[i:i + 1],
+                                             np.array([int(ctx[i])], np.int32), scale, k_scale,
+                                             v_scale)[0]
+    return out
+
+
 ORIGINAL_HASH = bm_oracle.block_hash
 ORIGINAL_ALLOCATE = bm_oracle.BlockManager.allocate
 ORIGINAL_APPEND = bm_oracle.BlockManager.append
@@ -179,6 +199,8 @@ MUTATIONS = {
     "fp8_dequant_ignores_scale": ("dequantize", lambda c, s: fp8_oracle.e4m3_decode(c)),
     "fp8_quant_multiplies": ("quantize", lambda b, s: fp8_oracle.e4m3_encode(
         oracle.bf16_to_f64(b) * np.float32(s))),
+    "fp8_prefill_swapped_scales": ("paged_prefill_fp8", _prefill_fp8_swapped_scales),
+    "fp8_prefill_not_causal": ("paged_prefill_fp8", _prefill_fp8_sees_whole_chunk),
     "bf16_shift_8": ("bf16_to_f64", lambda b: (np.asarray(b, np.uint16).astype(np.uint32) << 8)
                      .view(np.float32).astype(np.float64)),
 }

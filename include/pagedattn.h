@@ -12,7 +12,8 @@
  *   pa_paged_prefill   a chunk of new tokens over a cached prefix plus itself, causal
  *
  * plus pa_paged_gather, a test aid that un-pages a cache through the block tables,
- * and the FP8 cache variants pa_kvcache_store_fp8 / pa_paged_decode_fp8 (VLLM
+ * and the FP8 cache variants pa_kvcache_store_fp8 / pa_paged_decode_fp8 /
+ * pa_paged_prefill_fp8 (VLLM
  * 0.7.3 source article §5.3: the KV cache may be kept in FP8 while the
  * attention output stays in high precision).
  *
@@ -196,6 +197,26 @@ int pa_paged_decode_append_fp8(const void* q, const void* k_new, const void* v_n
                                float scale, float k_scale, float v_scale, void* out,
                                int out_dtype, void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/*
+ * Prefix-hit prefill on FP8 pools (layout above).  The chunk's own tokens must
+ * already be in the cache (stored by pa_kvcache_store_fp8 with the same
+ * scales: a step stores before it attends, MinivLLM guide §4.6), so every key
+ * 0 .. context_lens[i]-1 of sequence i is read through its block table: chunk
+ * token t (absolute position P + t, P = context_lens[i] - q_len) attends to
+ * keys 0 .. P + t with K = decode(code) * k_scale, V = decode(code) * v_scale.
+ * Codes are widened exactly to bf16, k_scale is folded into the score scale
+ * and v_scale multiplies the outputs; the MFMA arithmetic is that of
+ * pa_paged_prefill.  q, cu_seqlens_q, out, limits and errors as for
+ * pa_paged_prefill; k_scale and v_scale must be finite and > 0 (else
+ * PA_ERR_SHAPE).
+ */
+int pa_paged_prefill_fp8(const void* q, const int32_t* cu_seqlens_q, int num_seqs, int total_q,
+                         int max_q_len, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, int max_blocks_per_seq,
+                         const int32_t* context_lens, int num_q_heads, int num_kv_heads,
+                         int head_dim, int block_size, int num_blocks, float scale, float k_scale,
+                         float v_scale, void* out, int out_dtype, void* stream);
 
 /*
  * Graph-captured decode steps (MinivLLM guide §4.7: decode steps are captured

@@ -29,6 +29,7 @@ EXPORTED_SYMBOLS = (
     "pa_paged_decode_workspace_bytes",
     "pa_paged_decode",
     "pa_paged_prefill",
+    "pa_paged_prefill_fp8",
     "pa_paged_gather",
     "pa_kvcache_store_fp8",
     "pa_paged_decode_fp8_workspace_bytes",
@@ -87,6 +88,9 @@ def load_library() -> ctypes.CDLL:
     lib.pa_paged_decode.restype = I
     lib.pa_paged_prefill.argtypes = [P, P, P, P, I, I, I, P, P, P, I, P, I, I, I, I, I, F, P, I, P]
     lib.pa_paged_prefill.restype = I
+    lib.pa_paged_prefill_fp8.argtypes = [P, P, I, I, I, P, P, P, I, P, I, I, I, I, I, F, F, F, P, I,
+                                         P]
+    lib.pa_paged_prefill_fp8.restype = I
     lib.pa_paged_gather.argtypes = [P, P, I, P, P, I, I, I, I, I, I, P, P]
     lib.pa_paged_gather.restype = I
     lib.pa_kvcache_store_fp8.argtypes = [P, P, P, I, P, P, I, I, I, I, F, F, P]
@@ -363,6 +367,36 @@ def paged_prefill(q, k_new, v_new, cu_seqlens_q, block_tables, context_lens, out
         _ptr(v_cache), _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), Hq, Hkv,
         D, BS, NB, sc, _ptr(out), _out_dtype(out), _stream(q.device))
     _raise_on("pa_paged_prefill", rc)
+
+
+def paged_prefill_fp8(q, cu_seqlens_q, block_tables, context_lens, out, *, k_cache, v_cache,
+                      scale: Optional[float], k_scale: float, v_scale: float,
+                      max_q_len: Optional[int] = None) -> None:
+    """Prefix-hit prefill over uint8 E4M3 pools that already hold the chunk's own tokens:
+    every key 0 .. ctx-1 is read through the block table (keys code * k_scale, values
+    code * v_scale)."""
+    torch = _torch()
+    NB, BS, Hkv, D = _cache_geometry(k_cache, v_cache, torch.uint8)
+    _check(q, torch.bfloat16, "q", 3)
+    _check(cu_seqlens_q, torch.int32, "cu_seqlens_q", 1)
+    _check(block_tables, torch.int32, "block_tables", 2)
+    _check(context_lens, torch.int32, "context_lens", 1)
+    Tq, Hq, Dq = (int(x) for x in q.shape)
+    if Dq != D:
+        raise ValueError("q's head_dim disagrees with the cache")
+    B = int(context_lens.shape[0])
+    if cu_seqlens_q.shape[0] != B + 1 or block_tables.shape[0] != B:
+        raise ValueError("cu_seqlens_q must be [B+1] and block_tables [B, MBS]")
+    _check(out, out.dtype, "out", 3)
+    if tuple(out.shape) != (Tq, Hq, D):
+        raise ValueError(f"out must be [{Tq}, {Hq}, {D}]")
+    mq = Tq if max_q_len is None else int(max_q_len)
+    sc = float(scale) if scale is not None else 0.0
+    rc = load_library().pa_paged_prefill_fp8(
+        _ptr(q), _ptr(cu_seqlens_q), B, Tq, mq, _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        int(block_tables.shape[1]), _ptr(context_lens), Hq, Hkv, D, BS, NB, sc, float(k_scale),
+        float(v_scale), _ptr(out), _out_dtype(out), _stream(q.device))
+    _raise_on("pa_paged_prefill_fp8", rc)
 
 
 def paged_attention_mixed(q, k_new, v_new, slot_mapping, cu_seqlens_q, block_tables,

@@ -101,9 +101,10 @@ struct PrefillArgs {
   const int32_t* context_lens;
   void* out;
   int B, mbs, Hq, Hkv, group, bs_log2, num_blocks, out_f32, max_q_len;
-  float scale_log2e;
+  float scale_log2e;  // softmax scale (times the K scale of an FP8 cache) times log2(e)
+  float v_scale;      // V scale of an FP8 cache (1 for bf16)
 };
 
-int launch_paged_prefill(const PrefillArgs& args, int head_dim, hipStream_t stream);
+int launch_paged_prefill(const PrefillArgs& args, int head_dim, bool kv8, hipStream_t stream);
 
 }  // namespace pa

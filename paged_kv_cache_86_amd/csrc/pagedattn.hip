@@ -244,14 +244,22 @@ int pa_kvcache_store_fp8(const void* k, const void* v, const int32_t* slot_mappi
              : PA_ERR_HIP;
 }
 
-int pa_paged_prefill(const void* q, const void* k_new, const void* v_new,
-                     const int32_t* cu_seqlens_q, int num_seqs, int total_q, int max_q_len,
-                     const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                     int max_blocks_per_seq, const int32_t* context_lens, int num_q_heads,
-                     int num_kv_heads, int head_dim, int block_size, int num_blocks, float scale,
-                     void* out, int out_dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared argument checks and launch of both prefill forms (kv8: FP8 pools,
+// every key from the cache; otherwise bf16 pools, the chunk's keys from k_new / v_new).
+int prefill(const void* q, const void* k_new, const void* v_new, const int32_t* cu_seqlens_q,
+            int num_seqs, int total_q, int max_q_len, const void* k_cache, const void* v_cache,
+            const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+            int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+            float scale, bool kv8, float k_scale, float v_scale, void* out, int out_dtype,
+            void* stream) {
   if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || num_q_heads <= 0 ||
       max_blocks_per_seq <= 0)
+    return PA_ERR_SHAPE;
+  if (kv8 && !(k_scale > 0.f && isfinite(k_scale) && v_scale > 0.f && isfinite(v_scale)))
     return PA_ERR_SHAPE;
   int bs_log2 = 0;
   const int g = check_geometry(num_kv_heads, head_dim, block_size, num_blocks, &bs_log2);
@@ -260,8 +268,8 @@ int pa_paged_prefill(const void* q, const void* k_new, const void* v_new,
   if (out_dtype != PA_BF16 && out_dtype != PA_F32) return PA_ERR_UNSUPPORTED;
   if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX / 2) return PA_ERR_SHAPE;
   if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PA_OK;
-  if (!q || !k_new || !v_new || !cu_seqlens_q || !k_cache || !v_cache || !block_tables ||
-      !context_lens || !out)
+  if (!q || (!kv8 && (!k_new || !v_new)) || !cu_seqlens_q || !k_cache || !v_cache ||
+      !block_tables || !context_lens || !out)
     return PA_ERR_NULL;
   if (max_q_len > total_q) return PA_ERR_SHAPE;
 
@@ -284,10 +292,38 @@ int pa_paged_prefill(const void* q, const void* k_new, const void* v_new,
   a.num_blocks = num_blocks;
   a.out_f32 = out_dtype == PA_F32;
   a.max_q_len = max_q_len;
-  a.scale_log2e = resolve_scale(scale, head_dim) * pa::kLog2eHost;
-  const int rc = pa::launch_paged_prefill(a, head_dim, (hipStream_t)stream);
+  a.scale_log2e = resolve_scale(scale, head_dim) * (kv8 ? k_scale : 1.f) * pa::kLog2eHost;
+  a.v_scale = kv8 ? v_scale : 1.f;
+  const int rc = pa::launch_paged_prefill(a, head_dim, kv8, (hipStream_t)stream);
   if (rc == -3) return PA_ERR_UNSUPPORTED;
   return rc == 0 ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_paged_prefill(const void* q, const void* k_new, const void* v_new,
+                     const int32_t* cu_seqlens_q, int num_seqs, int total_q, int max_q_len,
+                     const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                     int max_blocks_per_seq, const int32_t* context_lens, int num_q_heads,
+                     int num_kv_heads, int head_dim, int block_size, int num_blocks, float scale,
+                     void* out, int out_dtype, void* stream) {
+  return prefill(q, k_new, v_new, cu_seqlens_q, num_seqs, total_q, max_q_len, k_cache, v_cache,
+                 block_tables, max_blocks_per_seq, context_lens, num_q_heads, num_kv_heads,
+                 head_dim, block_size, num_blocks, scale, false, 1.f, 1.f, out, out_dtype, stream);
+}
+
+int pa_paged_prefill_fp8(const void* q, const int32_t* cu_seqlens_q, int num_seqs, int total_q,
+                         int max_q_len, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, int max_blocks_per_seq,
+                         const int32_t* context_lens, int num_q_heads, int num_kv_heads,
+                         int head_dim, int block_size, int num_blocks, float scale, float k_scale,
+                         float v_scale, void* out, int out_dtype, void* stream) {
+  return prefill(q, nullptr, nullptr, cu_seqlens_q, num_seqs, total_q, max_q_len, k_cache, v_cache,
+                 block_tables, max_blocks_per_seq, context_lens, num_q_heads, num_kv_heads,
+                 head_dim, block_size, num_blocks, scale, true, k_scale, v_scale, out, out_dtype,
+                 stream);
 }
 
 int pa_paged_attention_mixed(const void* q, const void* k_new, const void* v_new,

@@ -61,7 +61,13 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{lo, hi}, bf16x2_t));
 }
 
-template <int D>
+// KV8 reads an FP8 (OCP E4M3) cache: the chunk's own tokens have been stored
+// into it already, so every key 0 .. ctx-1 comes through the block table; a
+// tile's codes are loaded into registers, widened exactly to bf16 (scale 1)
+// and written into the same swizzled LDS layout (so the MFMA part is
+// unchanged), one tile ahead of the compute; the K scale is folded into the
+// score scale and the V scale multiplies the outputs.
+template <int D, bool KV8>
 __global__ __launch_bounds__(256, 2) void paged_prefill_kernel(PrefillArgs a, int tt_tokens,
                                                             int ntt) {
   constexpr int KS = D / 16;                    // 16-wide K steps over head_dim
@@ -117,8 +123,12 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_kernel(PrefillArgs a, in
   for (int ks = 0; ks < KS; ++ks)
     qb[ks] = row_ok ? *(const u32x4*)(a.q + qrow + ks * 16 + hi * 8) : u32x4{0u, 0u, 0u, 0u};
 
-  // Stage the prefix's block ids (invalid ids become -1).
-  const int nblk = (P + (1 << a.bs_log2) - 1) >> a.bs_log2;
+  // Keys below `cached` come from the cache: the prefix, or (KV8) every key
+  // (never past the table's width; keys beyond it are masked out).
+  const int cached = KV8 ? min(kend, cap) : P;
+  const bool clipped = KV8 && kend > cached;
+  // Stage their block ids (invalid ids become -1).
+  const int nblk = (cached + (1 << a.bs_log2) - 1) >> a.bs_log2;
   const bool bt_in_lds = nblk <= kMaxBt;
   if (tid == 0) s_flags[0] = 0;
   __syncthreads();
@@ -138,7 +148,7 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_kernel(PrefillArgs a, in
   const int bs_mask = (1 << a.bs_log2) - 1;
   const int64_t kv_stride = (int64_t)a.Hkv * D;
   const int64_t head_off = (int64_t)kvh * D;
-  auto block_of = [&](int kk) __device__ -> int {
+  auto block_of = [&](int kk) -> int {
     if (bt_in_lds) return s_bt[kk >> a.bs_log2];
     const int b = a.block_tables[(int64_t)seq * a.mbs + (kk >> a.bs_log2)];
     return (b >= 0 && b < a.num_blocks) ? b : -1;
@@ -168,7 +178,7 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_kernel(PrefillArgs a, in
   // address plus the lane's fixed offset.  Otherwise each lane resolves its
   // own key; keys past kend or in an invalid block fetch the first new token's
   // row (valid, finite) and the softmax masks them.
-  auto issue_tile = [&](int j, int buf) __device__ {
+  auto issue_tile = [&](int j, int buf) {
     char* kdst = (char*)tiles + buf * BUFB;
     char* vdst = kdst + TB;
     const int k0 = j * kBN;
@@ -223,6 +233,51 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_kernel(PrefillArgs a, in
     }
   };
 
+  // KV8 tile loader: thread tid holds 16 codes (one 16-byte load) of rows
+  // tid / CPR8 + R8 i of the K and of the V tile, columns 16 (tid % CPR8) .. + 15;
+  // keys past `cached` or in an unmapped block get zero codes.
+  constexpr int CPR8 = D / 16;                 // 16-byte code chunks per row
+  constexpr int R8 = 256 / CPR8;               // rows per pass
+  constexpr int NP8 = KV8 ? kBN / R8 : 1;      // passes per tile
+  u32x4 k8r[NP8], v8r[NP8];
+  auto load_tile8 = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < NP8; ++i) {
+      const int kk = j * kBN + tid / CPR8 + R8 * i;
+      const int b = kk < cached ? block_of(kk) : -1;
+      const int64_t off = b < 0 ? 0
+          : (((int64_t)b << a.bs_log2) + (kk & bs_mask)) * kv_stride + head_off + (tid % CPR8) * 16;
+      const u32x4 kv = *(const u32x4*)((const char*)a.k_cache + off);
+      const u32x4 vv = *(const u32x4*)((const char*)a.v_cache + off);
+      k8r[i] = b < 0 ? u32x4{0u, 0u, 0u, 0u} : kv;
+      v8r[i] = b < 0 ? u32x4{0u, 0u, 0u, 0u} : vv;
+    }
+  };
+  auto store_tile8 = [&](int buf) {
+    char* kdst = (char*)tiles + buf * (4 * TILE);
+    char* vdst = kdst + TILE * 2;
+#pragma unroll
+    for (int i = 0; i < NP8; ++i) {
+      const int r = tid / CPR8 + R8 * i;
+      const int c0 = 2 * (tid % CPR8);
+      const u32x4 src[2] = {k8r[i], v8r[i]};
+      char* dst[2] = {kdst, vdst};
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const uint32_t w[4] = {src[t].x, src[t].y, src[t].z, src[t].w};
+        uint32_t bf[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bf[2 * e] = fp8x2_to_bf16x2<false>(w[e]);
+          bf[2 * e + 1] = fp8x2_to_bf16x2<true>(w[e]);
+        }
+        *(u32x4*)(dst[t] + r * D * 2 + ((c0 ^ swz<D>(r)) * 16)) = u32x4{bf[0], bf[1], bf[2], bf[3]};
+        *(u32x4*)(dst[t] + r * D * 2 + (((c0 + 1) ^ swz<D>(r)) * 16)) =
+            u32x4{bf[4], bf[5], bf[6], bf[7]};
+      }
+    }
+  };
+
   // Operand read offsets.  K operand of (kt, ks): row 32 kt + lr, chunk
   // 2 ks + hi; V^T operand of (s, dt, rd): row 16 s + 4 hi + 8 rd + i16 / 4,
   // element 32 dt + 16 ((lane >> 4) & 1) + 4 (i16 & 3).  The swizzle only
@@ -256,7 +311,7 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_kernel(PrefillArgs a, in
   float m_run = kNegBig;  // running max (raw score units) of this lane's row
   const float c = a.scale_log2e;
 
-  auto compute_tile = [&](int j, int bufoff) __device__ {
+  auto compute_tile = [&](int j, int bufoff) {
     // S^T = K Q^T for the two 32-key halves of the tile.
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
@@ -269,14 +324,14 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_kernel(PrefillArgs a, in
     }
     // Mask keys past this row's position (and keys of invalid blocks).
     const int k0 = j * kBN;
-    if (k0 + kBN - 1 > P + t0 || has_bad) {
+    if (k0 + kBN - 1 > P + t0 || has_bad || clipped) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int kk = k0 + kt * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-          bool ok = kk <= pos;
-          if (has_bad && kk < P) ok = ok && block_of(kk) >= 0;
+          bool ok = kk <= pos && (!clipped || kk < cached);
+          if (has_bad && kk < cached) ok = ok && block_of(kk) >= 0;
           sacc[kt][i] = ok ? sacc[kt][i] : -INFINITY;
         }
       }
@@ -338,12 +393,24 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_kernel(PrefillArgs a, in
   // The operand offsets point into buffer (j & 1): flipping the buffer bit of
   // every offset after each tile keeps the reads at "register + constant".
   // BUFB is a power of two larger than every in-buffer offset.
-  issue_tile(0, 0);
+  if constexpr (KV8) {
+    load_tile8(0);
+    store_tile8(0);
+  } else {
+    issue_tile(0, 0);
+  }
   for (int j = 0; j < ntiles; ++j) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile j are in LDS
-    __syncthreads();                     // ... and every wave's; the other buffer is free again
-    if (j + 1 < ntiles) issue_tile(j + 1, (j + 1) & 1);
+    if constexpr (!KV8)
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile j are in LDS
+    __syncthreads();                       // ... and every wave's; the other buffer is free again
+    if (j + 1 < ntiles) {
+      if constexpr (KV8) load_tile8(j + 1);
+      else issue_tile(j + 1, (j + 1) & 1);
+    }
     compute_tile(j, 0);
+    if constexpr (KV8) {
+      if (j + 1 < ntiles) store_tile8((j + 1) & 1);
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kofs[ks] ^= BUFB;
 #pragma unroll
@@ -355,7 +422,7 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_kernel(PrefillArgs a, in
 
   if (!row_ok) return;
   const float l_tot = lacc[0];
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float inv = (l_tot > 0.f ? 1.f / l_tot : 0.f) * (KV8 ? a.v_scale : 1.f);
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -377,7 +444,7 @@ constexpr size_t prefill_smem_bytes() {
   return (size_t)4 * kBN * D * sizeof(uint16_t) + (kMaxBt + 4) * sizeof(int);
 }
 
-template <int D>
+template <int D, bool KV8>
 int launch_prefill_d(const PrefillArgs& a, int tt_tokens, int ntt, int64_t nwg,
                      hipStream_t stream) {
   constexpr size_t smem = prefill_smem_bytes<D>();
@@ -387,27 +454,31 @@ int launch_prefill_d(const PrefillArgs& a, int tt_tokens, int ntt, int64_t nwg,
   if (hipGetDevice(&dev) != hipSuccess) return -1;
   const uint64_t bit = 1ull << (dev & 63);
   if (!(configured.load() & bit)) {
-    if (hipFuncSetAttribute((const void*)paged_prefill_kernel<D>,
+    if (hipFuncSetAttribute((const void*)paged_prefill_kernel<D, KV8>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
       return -1;
     configured.fetch_or(bit);
   }
-  hipLaunchKernelGGL(paged_prefill_kernel<D>, dim3((unsigned)nwg), dim3(256), smem, stream, a,
-                     tt_tokens, ntt);
+  hipLaunchKernelGGL((paged_prefill_kernel<D, KV8>), dim3((unsigned)nwg), dim3(256), smem, stream,
+                     a, tt_tokens, ntt);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 }  // namespace
 
-int launch_paged_prefill(const PrefillArgs& a, int head_dim, hipStream_t stream) {
+int launch_paged_prefill(const PrefillArgs& a, int head_dim, bool kv8, hipStream_t stream) {
   if (a.group > kRows) return -3;
   const int tt_tokens = kRows / a.group;
   const int ntt = (a.max_q_len + tt_tokens - 1) / tt_tokens;
   const int64_t nwg = (int64_t)ntt * a.B * a.Hkv;
   if (nwg == 0) return 0;
   if (nwg > INT32_MAX) return -2;
-  if (head_dim == 128) return launch_prefill_d<128>(a, tt_tokens, ntt, nwg, stream);
-  if (head_dim == 64) return launch_prefill_d<64>(a, tt_tokens, ntt, nwg, stream);
+  if (head_dim == 128)
+    return kv8 ? launch_prefill_d<128, true>(a, tt_tokens, ntt, nwg, stream)
+               : launch_prefill_d<128, false>(a, tt_tokens, ntt, nwg, stream);
+  if (head_dim == 64)
+    return kv8 ? launch_prefill_d<64, true>(a, tt_tokens, ntt, nwg, stream)
+               : launch_prefill_d<64, false>(a, tt_tokens, ntt, nwg, stream);
   return -3;
 }
 

@@ -113,6 +113,20 @@ def test_prefill_argument_checks(lib):
     assert prefill(lib, Tq=0, q=None) == PA_OK
 
 
+def test_prefill_fp8_argument_checks(lib):
+    def pf8(B=2, Tq=10, mq=5, q=FAKE, D=128, BS=16, Hq=4, Hkv=2, ks=0.5, vs=0.5):
+        return lib.pa_paged_prefill_fp8(q, FAKE, B, Tq, mq, FAKE, FAKE, FAKE, 8, FAKE, Hq, Hkv, D,
+                                        BS, 64, 0.0, ks, vs, FAKE, 0, None)
+    assert pf8(B=-1) == PA_ERR_SHAPE
+    assert pf8(mq=11) == PA_ERR_SHAPE
+    assert pf8(D=80) == PA_ERR_UNSUPPORTED
+    assert pf8(Hq=5) == PA_ERR_SHAPE
+    assert pf8(ks=0.0) == PA_ERR_SHAPE
+    assert pf8(vs=float("inf")) == PA_ERR_SHAPE
+    assert pf8(q=None) == PA_ERR_NULL
+    assert pf8(Tq=0, q=None) == PA_OK
+
+
 def test_gather_argument_checks(lib):
     def gather(B=2, maxc=40, cache=FAKE, BS=16):
         return lib.pa_paged_gather(cache, FAKE, 4, FAKE, FAKE, B, maxc, 2, 64, BS, 16, FAKE, None)

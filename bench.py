@@ -433,6 +433,33 @@ def main():
                 "tflops": round(tf, 2), "flops_per_launch": p.flops(),
                 "mfma_util": round(tf / MFMA_BF16_PEAK_TFS, 4),
                 "new_tokens_per_s": round(p.total_q / (pstep * 1e-3), 1)}
+            # the same chunk over FP8 pools holding the prefix and (stored first) the chunk
+            fscale = 1.0 / 64
+            NBp, BSp, Hkvp, Dp = p.k_cache.shape
+            pk8 = torch.empty((NBp, BSp, Hkvp, Dp), dtype=torch.uint8, device=dev)
+            pv8 = torch.empty_like(pk8)
+            every = torch.arange(NBp * BSp, dtype=torch.int32, device=dev)
+            pa.kvcache_store_fp8(pk.view(NBp * BSp, Hkvp, Dp), pv.view(NBp * BSp, Hkvp, Dp), every,
+                                 pk8, pv8, fscale, fscale)
+            del every
+
+            def pstore8():
+                pa.kvcache_store_fp8(pkn, pvn, pslots, pk8, pv8, fscale, fscale)
+
+            def prefill8():
+                pa.paged_prefill_fp8(pq, pcu, pbt, pctx, pout, k_cache=pk8, v_cache=pv8,
+                                     scale=p.scale, k_scale=fscale, v_scale=fscale, max_q_len=mq)
+
+            pstep8, pms8, pev8, _ = timed_loop(torch, pstore8, prefill8, max(10, args.steps // 2),
+                                               max(3, args.warmup // 2), flush)
+            tf8 = p.flops() / (pms8 * 1e-3) / 1e12
+            result["prefill"]["fp8"] = {
+                "workload": "same chunk, K/V cache in OCP FP8 E4M3 (per-tensor scale 1/64), the "
+                            "chunk stored into it first and read back through the table",
+                "ms": round(pms8, 5), "ms_step_incl_store": round(pstep8, 5),
+                "ms_per_call_events_median": round(float(np.median(pev8)), 5),
+                "tflops": round(tf8, 2), "mfma_util": round(tf8 / MFMA_BF16_PEAK_TFS, 4)}
+            del pk8, pv8
         except Exception as e:  # prefill not available: report, do not hide the decode result
             result["prefill"] = {"error": str(e)}
 

@@ -22,7 +22,10 @@
 //     reads (ds_read_b128) and the V^T operand reads (ds_read_b64_tr_b16, a
 //     transposing read) spread over the LDS banks;
 //   * O is rescaled only when a row's running max grows by more than 2^8
-//     (exp2 units), otherwise the stale max is kept.
+//     (exp2 units), otherwise the stale max is kept;
+//   * workgroups take their (token tile, sequence) items longest first (see
+//     ranked_item), which keeps the grid's tail short when cached prefixes
+//     differ in length.
 #include <atomic>
 
 #include "common.h"
@@ -61,6 +64,99 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{lo, hi}, bf16x2_t));
 }
 
+// Exclusive prefix sum of one int per thread over a 256-thread workgroup
+// (`tmp`: 4 ints of LDS used by this call only); `total` gets the sum.
+__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) tmp[w] = x;
+  __syncthreads();
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) base += i < w ? tmp[i] : 0;
+  total = tmp[0] + tmp[1] + tmp[2] + tmp[3];
+  return base + x - v;
+}
+
+// Work order of the prefill grid.  Workgroups are handed out roughly in
+// index order and the work per (token tile, sequence) item varies with the
+// sequence's cached prefix, so index order leaves a long tail; ranking the
+// items by the keys they walk, most first, and giving rank r to workgroups
+// r * Hkv .. r * Hkv + Hkv - 1 is the longest-processing-time-first list
+// schedule.  Every workgroup computes the ranking itself from the lengths in
+// device memory (a 256-bin histogram of tile counts, then two workgroup
+// scans), which costs O(items / 256) per thread, so it is used up to
+// kOrderMaxItems items and index order beyond.
+constexpr int kOrderBins = 256;
+constexpr int kOrderMaxItems = 4096;
+
+// Priority bin of item i = seq * ntt + tt (0 = most keys to walk).
+__device__ __forceinline__ int order_bin(const PrefillArgs& a, int i, int ntt, int tt_tokens,
+                                         int cap, int shift) {
+  const int seq = i / ntt;
+  const int tt = i - seq * ntt;
+  const int qa = a.cu_seqlens_q[seq];
+  const int n = a.cu_seqlens_q[seq + 1] - qa;
+  const int t0 = tt * tt_tokens;
+  if (n <= 0 || t0 >= n) return kOrderBins - 1;
+  int P = a.context_lens[seq] - n;
+  P = P < 0 ? 0 : (P > cap ? cap : P);
+  const int tiles = (P + min(t0 + tt_tokens, n) + 63) >> 6;
+  return kOrderBins - 1 - min(tiles >> shift, kOrderBins - 1);
+}
+
+// The (token tile, sequence) item of rank r when items are ordered by the
+// keys they walk, most first, ties by index.  s: 256 + 16 ints of LDS.
+__device__ void ranked_item(const PrefillArgs& a, int ntt, int tt_tokens, int r, int* s,
+                            int& tt_out, int& seq_out) {
+  const int tid = threadIdx.x;
+  const int M = a.B * ntt;
+  const int per = (M + 255) >> 8;
+  const int i0 = min(tid * per, M), i1 = min(i0 + per, M);
+  const int cap = a.mbs << a.bs_log2;
+  const int64_t maxtiles = ((int64_t)cap + a.max_q_len + 63) >> 6;
+  int shift = 0;
+  while ((maxtiles >> shift) >= kOrderBins) ++shift;
+  int* hist = s;
+  int* sel = s + kOrderBins;  // [0..3] scan 1, [4..7] scan 2, [8] bin, [9] offset, [10] item
+  hist[tid] = 0;
+  if (tid == 0) sel[10] = 0;  // a valid item whatever happens below
+  __syncthreads();
+  for (int i = i0; i < i1; ++i) atomicAdd(&hist[order_bin(a, i, ntt, tt_tokens, cap, shift)], 1);
+  __syncthreads();
+  const int h = hist[tid];
+  int total;
+  const int start = block_excl_scan(h, sel, total);
+  if (r >= start && r < start + h) {
+    sel[8] = tid;
+    sel[9] = r - start;
+  }
+  __syncthreads();
+  const int bin = sel[8];
+  const int off = sel[9];
+  int cnt = 0;
+  for (int i = i0; i < i1; ++i) cnt += order_bin(a, i, ntt, tt_tokens, cap, shift) == bin;
+  const int before = block_excl_scan(cnt, sel + 4, total);
+  if (off >= before && off < before + cnt) {
+    int k = off - before;
+    for (int i = i0; i < i1; ++i) {
+      if (order_bin(a, i, ntt, tt_tokens, cap, shift) == bin) {
+        if (k == 0) { sel[10] = i; break; }
+        --k;
+      }
+    }
+  }
+  __syncthreads();
+  const int item = sel[10];
+  seq_out = item / ntt;
+  tt_out = item - seq_out * ntt;
+}
+
 // KV8 reads an FP8 (OCP E4M3) cache: the chunk's own tokens have been stored
 // into it already, so every key 0 .. ctx-1 comes through the block table; a
 // tile's codes are loaded into registers, widened exactly to bf16 (scale 1)
@@ -69,7 +165,7 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 // score scale and the V scale multiplies the outputs.
 template <int D, bool KV8>
 __global__ __launch_bounds__(256, 2) void paged_prefill_kernel(PrefillArgs a, int tt_tokens,
-                                                            int ntt) {
+                                                            int ntt, int ranked) {
   constexpr int KS = D / 16;                    // 16-wide K steps over head_dim
   constexpr int DT = D / 32;                    // 32-row tiles of O^T
   constexpr int CPR = D / 8;                    // 16-byte chunks per K/V row
@@ -88,14 +184,21 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_kernel(PrefillArgs a, in
   const int lr = lane & 31;  // this lane's query row within the wave
   const int hi = lane >> 5;  // which half of a 16-wide K step
 
-  // Heaviest token tiles first (later tiles attend to more keys).  The token
-  // tiles of one (sequence, KV head) are B * Hkv workgroups apart, so they
-  // land on one XCD when B * Hkv is a multiple of 8 and share its L2.
-  const int per_tt = a.B * a.Hkv;
-  const int tt = ntt - 1 - (int)(blockIdx.x / per_tt);
-  const int rem = blockIdx.x % per_tt;
-  const int seq = rem / a.Hkv;
-  const int kvh = rem - seq * a.Hkv;
+  // Items in rank order (see ranked_item), else the last token tiles first
+  // (later tiles attend to more keys).  Either way the workgroups of one
+  // (sequence, KV head) are a multiple of Hkv apart, so they land on one XCD
+  // when Hkv is a multiple of 8 and share its L2.
+  int tt, seq, kvh;
+  if (ranked) {
+    kvh = (int)(blockIdx.x % a.Hkv);
+    ranked_item(a, ntt, tt_tokens, (int)(blockIdx.x / a.Hkv), (int*)smem, tt, seq);
+  } else {
+    const int per_tt = a.B * a.Hkv;
+    tt = ntt - 1 - (int)(blockIdx.x / per_tt);
+    const int rem = blockIdx.x % per_tt;
+    seq = rem / a.Hkv;
+    kvh = rem - seq * a.Hkv;
+  }
 
   const int qa = a.cu_seqlens_q[seq];
   const int n = a.cu_seqlens_q[seq + 1] - qa;
@@ -447,6 +550,7 @@ constexpr size_t prefill_smem_bytes() {
 template <int D, bool KV8>
 int launch_prefill_d(const PrefillArgs& a, int tt_tokens, int ntt, int64_t nwg,
                      hipStream_t stream) {
+  const int ranked = (int64_t)a.B * ntt <= kOrderMaxItems;
   constexpr size_t smem = prefill_smem_bytes<D>();
   // More than 64 KiB of dynamic LDS must be allowed once per device.
   static std::atomic<uint64_t> configured{0};
@@ -460,7 +564,7 @@ int launch_prefill_d(const PrefillArgs& a, int tt_tokens, int ntt, int64_t nwg,
     configured.fetch_or(bit);
   }
   hipLaunchKernelGGL((paged_prefill_kernel<D, KV8>), dim3((unsigned)nwg), dim3(256), smem, stream,
-                     a, tt_tokens, ntt);
+                     a, tt_tokens, ntt, ranked);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -121,3 +121,40 @@ def test_prefill_last_row_equals_decode():
     dec = torch.empty((p.batch, p.num_q_heads, p.head_dim), dtype=torch.float32, device=dev)
     pa.paged_decode(q_last, d.k_cache, d.v_cache, d.tables, d.ctx, p.scale, dec)
     assert (out[torch.from_numpy(last).to(dev)] - dec).abs().max().item() <= 2e-3
+
+
+def test_prefill_item_order_does_not_change_results():
+    """Items run longest first up to 4096 (token tile, sequence) items and in index order
+    beyond: a max_q_len that takes the grid past that limit (the extra tiles exit) gives
+    bit-identical outputs."""
+    dev = device()
+    rng = np.random.default_rng(57)
+    B = 260
+    p = prefill_case(57, rng.integers(0, 41, B), rng.integers(1, 4, B), 16, 1, 64, 16)
+    d = PrefillOnDevice(p, dev)
+    tt_tokens = 128 // (p.num_q_heads // p.num_kv_heads)
+    big = p.total_q
+    assert B * ((int(p.q_lens.max()) + tt_tokens - 1) // tt_tokens) <= 4096
+    assert B * ((big + tt_tokens - 1) // tt_tokens) > 4096
+    say(f"[prefill-order] B={B} max_q_len {int(p.q_lens.max())} vs {big}")
+    ranked = d.run(torch.float32)
+    indexed = d.run(torch.float32, max_q_len=big)
+    assert torch.equal(ranked, indexed)
+    ref = oracle.paged_prefill(p.q, p.k_new, p.v_new, p.cu_seqlens_q, p.k_cache, p.v_cache,
+                               p.block_tables, p.context_lens, np.float32(p.scale))
+    assert np.abs(as_f64(ranked) - ref).max() <= ATOL
+
+
+def test_prefill_many_sequences():
+    """4100 short chunks (more items than the ranked order takes) against the oracle."""
+    dev = device()
+    rng = np.random.default_rng(58)
+    B = 4100
+    P = rng.integers(0, 41, B)
+    n = rng.integers(1, 4, B)
+    p = prefill_case(58, P, n, 2, 1, 64, 16)
+    say(f"[prefill-many] B={B} Tq={p.total_q}")
+    out = as_f64(PrefillOnDevice(p, dev).run(torch.float32))
+    ref = oracle.paged_prefill(p.q, p.k_new, p.v_new, p.cu_seqlens_q, p.k_cache, p.v_cache,
+                               p.block_tables, p.context_lens, np.float32(p.scale))
+    assert np.abs(out - ref).max() <= ATOL

@@ -13,9 +13,10 @@
 //     KV head (GQA rows share every K/V tile) and walks 64-key tiles;
 //   * S^T = K Q^T and O^T = V^T P^T: the accumulator layout gives each lane one
 //     query row, so the softmax is per lane (plus one exchange with the lane
-//     holding the row's other 32 keys) and P feeds the second MFMA from
-//     registers; the softmax denominator comes from a third MFMA against a
-//     matrix of ones, so it sums exactly the bf16 weights the PV product uses;
+//     holding the row's other 32 keys, v_permlane32_swap) and P feeds the
+//     second MFMA from registers; the softmax denominator sums exactly the
+//     bf16 weights the PV product uses (v_dot2_f32_bf16 against ones, each
+//     lane over its half of the keys, the halves added at the end);
 //   * K and V tiles go straight from global memory to LDS
 //     (global_load_lds_dwordx4), double-buffered, one barrier per tile; rows are
 //     stored with their 16-byte chunks XOR-swizzled so that both the K operand
@@ -62,6 +63,17 @@ __device__ __forceinline__ int swz(int r) {
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{lo, hi}, bf16x2_t));
+}
+
+// Max and sum of a value over lanes l and l ^ 32 (v_permlane32_swap exchanges
+// the two halves of the wave).
+__device__ __forceinline__ float halves_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Exclusive prefix sum of one int per thread over a 256-thread workgroup
@@ -409,22 +421,37 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_kernel(PrefillArgs a, in
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
-  f32x16 lacc = f32x16{};
-  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0
+  float l_part = 0.f;  // this lane's half of the row's softmax denominator
   float m_run = kNegBig;  // running max (raw score units) of this lane's row
   const float c = a.scale_log2e;
 
   auto compute_tile = [&](int j, int bufoff) {
     // S^T = K Q^T for the two 32-key halves of the tile.
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    u32x4 ka[KS][2];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const u32x4 ka = *(const u32x4*)(lds + bufoff + kofs[ks] + kt * 32 * D * 2);
-        sacc[kt] = mfma32(ka, qb[ks], sacc[kt]);
-      }
+      for (int kt = 0; kt < 2; ++kt) ka[ks][kt] = *(const u32x4*)(lds + bufoff + kofs[ks] + kt * 32 * D * 2);
     }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) sacc[kt] = mfma32(ka[ks][kt], qb[ks], sacc[kt]);
+    }
+    // Keep 8 K operand reads in flight ahead of the MFMAs (left alone, the
+    // scheduler waits on each pair of reads before its two MFMAs; all 16
+    // ahead does not fit in the registers of two waves per SIMD).
+    constexpr int kAhead = 2 * KS < 8 ? 2 * KS : 8;
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+#pragma unroll
+    for (int i = 0; i < 2 * KS - kAhead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     // Mask keys past this row's position (and keys of invalid blocks).
     const int k0 = j * kBN;
     if (k0 + kBN - 1 > P + t0 || has_bad || clipped) {
@@ -445,7 +472,7 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_kernel(PrefillArgs a, in
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
     }
-    mx = fmaxf(mx, shfl_xor(mx, 32));
+    mx = halves_max(mx);
     // Lazy rescale: keep the stale max unless it grew by more than 2^8.
     const bool grow = (mx - m_run) * c > kRescaleLog2;
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
@@ -454,7 +481,7 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_kernel(PrefillArgs a, in
       m_run = m_new;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
-      lacc *= alpha;
+      l_part *= alpha;
     }
     const float mc = m_run * c;
     u32x4 pb[4];  // P^T operands of the four 16-key steps, bf16
@@ -469,7 +496,7 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_kernel(PrefillArgs a, in
       }
       pb[s4] = u32x4{wv[0], wv[1], wv[2], wv[3]};
     }
-    // O^T += V^T P^T and l += 1^T P^T.  The V^T operand of lane l is column
+    // O^T += V^T P^T and l += the same bf16 weights.  The V^T operand of lane l is column
     // 32 dt + (l & 31) at keys 16 s + {4 hi .. 4 hi + 3, 8 + 4 hi .. 8 + 4 hi + 3},
     // gathered by two transposing reads: source lane i of a 16-lane group reads
     // row (kb + i / 4), elements dbase + 4 (i % 4) .. + 3.
@@ -489,7 +516,8 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_kernel(PrefillArgs a, in
                                                             part[1][2], part[1][3]});
         oacc[dt] = mfma32(va, pb[s4], oacc[dt]);
       }
-      lacc = mfma32(ones, pb[s4], lacc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) l_part = dot2_bf16(pb[s4][e], 0x3F803F80u, l_part);
     }
   };
 
@@ -523,8 +551,8 @@ __global__ __launch_bounds__(256, 2) void paged_prefill_kernel(PrefillArgs a, in
     }
   }
 
+  const float l_tot = halves_sum(l_part);
   if (!row_ok) return;
-  const float l_tot = lacc[0];
   const float inv = (l_tot > 0.f ? 1.f / l_tot : 0.f) * (KV8 ? a.v_scale : 1.f);
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {

@@ -45,6 +45,7 @@ def parse():
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-mixed", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read probe")
     ap.add_argument("--no-other", action="store_true", help="skip the 7B-shaped and "
                     "max-concurrency decode legs")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -274,6 +275,30 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": alg},
     }
+
+    # ---------------------------------------------------------------- streaming-read ceiling
+    # The practical ceiling of a bandwidth-bound kernel on this device: one plain read of a
+    # 1 GiB buffer (four times the last-level cache), event-timed, next to the spec peak.
+    if not args.no_ceiling:
+        probe_src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            pa.stream_read(probe_src, sink)
+        pe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        n_probe = 20
+        torch.cuda.synchronize()
+        pe[0].record()
+        for _ in range(n_probe):
+            pa.stream_read(probe_src, sink)
+        pe[1].record()
+        torch.cuda.synchronize()
+        probe_ms = pe[0].elapsed_time(pe[1]) / n_probe
+        ceil_gbs = (1 << 30) / (probe_ms * 1e-3) / 1e9
+        result["stream_read_ceiling"] = {
+            "kernel": "stream_read_kernel (pa_stream_read, 1 GiB, non-temporal 16-byte loads)",
+            "gb_s": round(ceil_gbs, 1), "frac_hbm_peak": round(ceil_gbs / HBM_PEAK_GBS, 4),
+            "headline_frac_of_ceiling": round(achieved / ceil_gbs, 4)}
+        del probe_src, sink
 
     # ---------------------------------------------------------------- other decode shapes
     if not args.no_other:

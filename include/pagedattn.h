@@ -341,6 +341,19 @@ int pa_paged_gather(const void* cache, const int32_t* block_tables, int max_bloc
                     int num_blocks, void* out, void* stream);
 
 /*
+ * Measurement aid: reads `bytes` bytes at `src` (device) once, in contiguous
+ * 32 KiB runs per workgroup with non-temporal 16-byte loads; a timed call
+ * gives the device's streaming-read rate, the practical ceiling of the
+ * bandwidth-bound decode next to the HBM spec peak.  Not part of the
+ * attention path.
+ *   src    16-byte aligned, bytes a multiple of 16 (else PA_ERR_SHAPE)
+ *   sink   4 bytes of device memory, 4-byte aligned, that the kernel may
+ *          overwrite (it keeps the loads live; the value means nothing)
+ * Asynchronous on `stream`; bytes == 0 is a no-op.
+ */
+int pa_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
+/*
  * Host block manager with prefix caching (MinivLLM guide Step 3 §3.2 Block,
  * §3.3 BlockManager; Step 4 §4.5 prepare_prefill / prepare_decode).  Host
  * memory only, no GPU calls; not thread-safe (one caller at a time per

@@ -31,6 +31,7 @@ EXPORTED_SYMBOLS = (
     "pa_paged_prefill",
     "pa_paged_prefill_fp8",
     "pa_paged_gather",
+    "pa_stream_read",
     "pa_kvcache_store_fp8",
     "pa_paged_decode_fp8_workspace_bytes",
     "pa_paged_decode_fp8",
@@ -93,6 +94,8 @@ def load_library() -> ctypes.CDLL:
     lib.pa_paged_prefill_fp8.restype = I
     lib.pa_paged_gather.argtypes = [P, P, I, P, P, I, I, I, I, I, I, P, P]
     lib.pa_paged_gather.restype = I
+    lib.pa_stream_read.argtypes = [P, Z, P, P]
+    lib.pa_stream_read.restype = I
     lib.pa_kvcache_store_fp8.argtypes = [P, P, P, I, P, P, I, I, I, I, F, F, P]
     lib.pa_kvcache_store_fp8.restype = I
     lib.pa_paged_decode_fp8_workspace_bytes.argtypes = [I, I, I, I, I, I]
@@ -457,6 +460,18 @@ def paged_gather(cache, block_tables, context_lens, cu_seqlens_k, max_context_le
         _ptr(cu_seqlens_k), B, int(max_context_len), Hkv, D, BS, NB, _ptr(out),
         _stream(cache.device))
     _raise_on("pa_paged_gather", rc)
+
+
+def stream_read(src, sink) -> None:
+    """Measurement aid: read every byte of `src` once (see pa_stream_read); `sink` is a
+    device tensor of at least 4 bytes that the kernel may overwrite."""
+    if not (src.is_cuda and src.is_contiguous() and sink.is_cuda and sink.is_contiguous()):
+        raise ValueError("stream_read: src and sink must be contiguous device tensors")
+    if sink.numel() * sink.element_size() < 4:
+        raise ValueError("stream_read: sink must hold at least 4 bytes")
+    rc = load_library().pa_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                       _stream(src.device))
+    _raise_on("pa_stream_read", rc)
 
 
 def default_scale(head_dim: int) -> float:

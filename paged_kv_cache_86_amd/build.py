@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpagedattn.so")
 SOURCES = ["pagedattn.hip", "store_gather.hip", "decode.hip", "decode_mfma.hip", "prefill.hip",
-           "graph.hip", "block_manager.cpp"]
+           "graph.hip", "probe.hip", "block_manager.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CXX = os.environ.get("CXX", "g++")

@@ -107,4 +107,6 @@ struct PrefillArgs {
 
 int launch_paged_prefill(const PrefillArgs& args, int head_dim, bool kv8, hipStream_t stream);
 
+int launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 }  // namespace pa

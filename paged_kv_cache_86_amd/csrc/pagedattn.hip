@@ -422,4 +422,12 @@ int pa_paged_gather(const void* cache, const int32_t* block_tables, int max_bloc
              : PA_ERR_HIP;
 }
 
+int pa_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (bytes == 0) return PA_OK;
+  if (!src || !sink) return PA_ERR_NULL;
+  if (bytes % 16 != 0 || ((uintptr_t)src & 15) != 0 || ((uintptr_t)sink & 3) != 0)
+    return PA_ERR_SHAPE;
+  return pa::launch_stream_read(src, bytes, sink, (hipStream_t)stream) == 0 ? PA_OK : PA_ERR_HIP;
+}
+
 }  // extern "C"

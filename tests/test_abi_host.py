@@ -136,6 +136,17 @@ def test_gather_argument_checks(lib):
     assert gather(B=0, cache=None) == PA_OK
 
 
+def test_stream_read_argument_checks(lib):
+    def probe(src=FAKE, nbytes=4096, sink=FAKE):
+        return lib.pa_stream_read(src, nbytes, sink, None)
+    assert probe(nbytes=0, src=None) == PA_OK
+    assert probe(src=None) == PA_ERR_NULL
+    assert probe(sink=None) == PA_ERR_NULL
+    assert probe(nbytes=4100) == PA_ERR_SHAPE
+    assert probe(src=ctypes.c_void_p(0x1008)) == PA_ERR_SHAPE
+    assert probe(sink=ctypes.c_void_p(0x1002)) == PA_ERR_SHAPE
+
+
 def test_python_binding_rejects_cpu_tensors():
     import torch
     k = torch.zeros(2, 1, 64, dtype=torch.bfloat16)

@@ -285,3 +285,29 @@ def test_decode_long_splits(D, BS):
     say(f"[decode-long] D={D} BS={BS}: max|err| {err:.3e}")
     assert err <= ATOL
     check_append(c, dev, f"long splits D{D} BS{BS}")
+
+
+MAX_CASES = [(128, 2), (128, 7), (64, 2), (64, 7)]  # VALU (2 heads per KV head) and MFMA (7)
+
+
+@pytest.mark.parametrize("D,Hq", MAX_CASES, ids=[f"D{d}_h{h}-1" for d, h in MAX_CASES])
+def test_decode_max_context(D, Hq):
+    """The longest context one decode call takes (256 short splits: 65,536 tokens, or 131,072 on
+    the head_dim-64 VALU kernel, whose splits are 512 tokens) with a table exactly that wide,
+    next to one-token and short contexts; store then decode, and the fused call."""
+    dev = device()
+    S = 512 if (D == 64 and Hq == 2) else 256
+    maxc, BS = 256 * S, 256
+    ctx = [maxc, 1, maxc - 1, 300]
+    c = decode_case(9100 + D + Hq, ctx, Hq, 1, D, BS, nb_factor=1.05, max_blocks_per_seq=maxc // BS)
+    assert pa.decode_workspace_bytes(c.batch, Hq, 1, D, BS, c.max_blocks_per_seq) > 0
+    say(f"[decode-max] D={D} h={Hq}/1 ctx={ctx}")
+    d = DecodeOnDevice(c, dev)
+    d.store()
+    out32 = as_f64(d.decode(torch.float32))
+    kc, vc = oracle.kvcache_store(c.k_new, c.v_new, c.slot_mapping, c.k_cache, c.v_cache)
+    ref = oracle.paged_decode(c.q, kc, vc, c.block_tables, c.context_lens, np.float32(c.scale))
+    err = np.abs(out32 - ref).max()
+    say(f"[decode-max] D={D} h={Hq}/1: max|err| {err:.3e}")
+    assert err <= ATOL
+    check_append(c, dev, f"max context D{D} h{Hq}/1")

@@ -101,6 +101,7 @@ SMALL = [
     (128, 32, 2, 2, [513, 31], [129, 128]),        # G = 1
     (128, 1, 4, 4, [65, 0], [70, 1]),              # block size 1
     (64, 1024, 6, 2, [1100, 5], [300, 77]),        # block size 1024, G = 3
+    (64, 16, 4, 2, [17000, 16383, 5], [70, 2, 130]),  # more than the 1024 block ids staged in LDS
 ]
 
 

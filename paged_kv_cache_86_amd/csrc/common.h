@@ -99,4 +99,65 @@ __device__ __forceinline__ float shfl_xor(float v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
 
+// Compacted decode work list.  The (sequence, split) items of a decode call,
+// sequences in order and each sequence's splits in order, where a sequence of
+// context ctx (clamped to [0, cap]) has max(1, ceil(ctx / S)) splits, or
+// ceil(ctx / 2S) when long splits are on and it needs more than nsplit_max
+// short ones.  Finds item `item` for the calling wave: lane l counts the
+// splits of sequences l*k .. l*k+k-1 (k = ceil(B / 64) <= PER_LANE), a wave
+// scan turns the counts into each lane's first item, and the lane holding
+// `item` walks its sequences.  Every lane returns the same result; false when
+// `item` is past the last item.
+template <int PER_LANE, class Args>
+__device__ __forceinline__ bool decode_work_item(const Args& a, int item, int S, bool long_ok,
+                                                 int& seq, int& split) {
+  const int lane = threadIdx.x & 63;
+  const int B = a.batch;
+  const int k = (B + 63) >> 6;
+  const int s0 = lane * k;
+  const int cap = a.mbs << a.bs_log2;
+  int cnt[PER_LANE];
+  int ctxs[PER_LANE];
+#pragma unroll
+  for (int j = 0; j < PER_LANE; ++j) ctxs[j] = (j < k && s0 + j < B) ? a.context_lens[s0 + j] : 0;
+  int tot = 0;
+#pragma unroll
+  for (int j = 0; j < PER_LANE; ++j) {
+    int n = 0;
+    if (j < k && s0 + j < B) {
+      const int ctx = ctxs[j] < 0 ? 0 : (ctxs[j] > cap ? cap : ctxs[j]);
+      const int nshort = ctx == 0 ? 1 : (ctx + S - 1) / S;
+      n = (long_ok && nshort > a.nsplit_max) ? (ctx + 2 * S - 1) / (2 * S) : nshort;
+    }
+    cnt[j] = n;
+    tot += n;
+  }
+  int incl = tot;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
+  }
+  const int excl = incl - tot;
+  const bool mine = item >= excl && item < incl;
+  const uint64_t bal = __builtin_amdgcn_ballot_w64(mine);
+  if (bal == 0) return false;
+  int fs = 0, fsplit = 0;
+  if (mine) {
+    int rem = item - excl;
+#pragma unroll
+    for (int j = 0; j < PER_LANE; ++j) {
+      if (rem >= 0 && rem < cnt[j]) {
+        fs = s0 + j;
+        fsplit = rem;
+      }
+      rem -= cnt[j];
+    }
+  }
+  const int src = (int)__builtin_ctzll(bal);
+  seq = __builtin_amdgcn_readlane(fs, src);
+  split = __builtin_amdgcn_readlane(fsplit, src);
+  return true;
+}
+
 }  // namespace pa

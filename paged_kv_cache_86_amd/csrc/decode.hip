@@ -20,7 +20,12 @@
 //     context that fits in one split writes its output directly;
 //   * splits come in two lengths when the grid is large enough: a context
 //     that would need more short splits than the grid has slots per sequence
-//     takes splits of twice the length instead.  The
+//     takes splits of twice the length instead;
+//   * the grid has a slot for every split of the longest possible context
+//     (the host does not know the lengths); for batches of up to 256
+//     sequences each workgroup looks its (sequence, split) up in the
+//     compacted list of the splits that exist, so the empty slots end up at
+//     the end of the grid instead of between the real ones.  The
 //     kernel boundary is what makes one XCD's partials visible to another:
 //     an in-kernel "last workgroup merges" scheme needs a device-scope
 //     release/acquire per workgroup, which on this chip writes back and
@@ -89,10 +94,19 @@ __device__ __forceinline__ void paged_decode_body(const DecodeArgs& a) {
   constexpr int NLB = D / 8;  // 16-byte bf16 vectors per new K (or V) row of one head
 
   const int bid = blockIdx.x;
-  const int hg = bid % a.hg;
-  const int rest = bid / a.hg;
-  const int split = rest % a.nsplit_max;
-  const int seq = rest / a.nsplit_max;
+  int hg, split, seq;
+  if (a.compact) {
+    // Item bid / hg of the compacted list (its head groups on consecutive
+    // workgroups, as in index order); workgroups past the last item exit.
+    const int item = bid / a.hg;
+    hg = bid - item * a.hg;
+    if (!decode_work_item<kCompactPerLane>(a, item, S, LONG, seq, split)) return;
+  } else {
+    hg = bid % a.hg;
+    const int rest = bid / a.hg;
+    split = rest % a.nsplit_max;
+    seq = rest / a.nsplit_max;
+  }
   const int kvh = hg / a.nsub;
   const int sub = hg - kvh * a.nsub;
   const int h0 = kvh * a.group + sub * GT;
@@ -720,6 +734,7 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int head_dim, int block_size, int
   p.long_splits = !p.mfma && block_size >= S && p.nsplit_short >= kLongSplitMinShort &&
                   units * half >= kLongSplitMinGrid;
   p.nsplit_max = p.long_splits ? (int)half : p.nsplit_short;
+  p.compact = B <= kCompactMaxSeqs;
   const int64_t parts = units * p.nsplit_max * p.gt;
   auto round256 = [](size_t x) { return (x + 255) / 256 * 256; };
   p.units = units;

@@ -99,10 +99,21 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
   __shared__ float s_l[kW][kQR];
 
   const int bid = blockIdx.x;
-  const int hg = bid % a.hg;
-  const int rest = bid / a.hg;
-  const int split = rest % a.nsplit_max;
-  const int seq = rest / a.nsplit_max;
+  int hg, split, seq;
+  // Compacted items as in the VALU kernel; not in the bf16 fused-store
+  // variant with block ids in scalars, which is at its 168-register limit
+  // without the lookup.
+  constexpr bool kCompactOk = KV8 || !APPEND || !SCALAR_BLK;
+  if (kCompactOk && a.compact) {
+    const int item = bid / a.hg;
+    hg = bid - item * a.hg;
+    if (!decode_work_item<kCompactPerLane>(a, item, S, false, seq, split)) return;
+  } else {
+    hg = bid % a.hg;
+    const int rest = bid / a.hg;
+    split = rest % a.nsplit_max;
+    seq = rest / a.nsplit_max;
+  }
   const int kvh = hg / a.nsub;
   const int sub = hg - kvh * a.nsub;
   const int gt = (a.group + a.nsub - 1) / a.nsub;  // heads per sub-group (partial stride)

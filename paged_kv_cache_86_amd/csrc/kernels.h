@@ -20,6 +20,12 @@ constexpr int kLongSplitMinShort = 8;
 // ... and the grid with half the slots per sequence still has this many
 // workgroups (32 per compute unit of a 256-CU device).
 constexpr int64_t kLongSplitMinGrid = 8192;
+// Decode grids of up to this many sequences take their (sequence, split)
+// items from a compacted list (4 sequences per lane of one wave in the
+// lookup); larger batches keep index order, where the lookup's extra round
+// trip costs more than the empty workgroups it removes (measured at 512).
+constexpr int kCompactPerLane = 4;
+constexpr int kCompactMaxSeqs = 64 * kCompactPerLane;
 // Query heads per KV head from which decode runs on MFMA (bf16 and FP8
 // pools), the most heads one MFMA workgroup serves, and its split length.
 constexpr int kMfmaMinGroup = 3;
@@ -46,6 +52,7 @@ struct DecodePlan {
   bool long_splits;  // contexts above nsplit_max short splits use splits of twice the length
   int nsplit_max;    // workgroups (and partial slots) per (sequence, head group)
   bool mfma;         // the MFMA kernel (bf16 pools, large query-head groups)
+  bool compact;      // workgroups take compacted (sequence, split) items
   int64_t units;   // (sequence, head group) pairs
   size_t ml_bytes, o_bytes;  // workspace regions: (max, sum) pairs, then unnormalised outputs
   size_t workspace_bytes() const { return ml_bytes + o_bytes; }
@@ -65,6 +72,8 @@ struct DecodeArgs {
   float* ws_o;
   int mbs, Hq, Hkv, group, nsub, hg, bs_log2, split_log2, nsplit_max, num_blocks, out_f32;
   int long_splits;    // see DecodePlan
+  int batch;          // sequences (B)
+  int compact;        // see DecodePlan
   float scale_log2e;  // softmax scale (times the K scale of an FP8 cache) times log2(e)
   float v_scale;      // V scale of an FP8 cache (1 for bf16)
   // Fused store of the new token (append variants only; unused otherwise).

@@ -311,3 +311,51 @@ def test_decode_max_context(D, Hq):
     say(f"[decode-max] D={D} h={Hq}/1: max|err| {err:.3e}")
     assert err <= ATOL
     check_append(c, dev, f"max context D{D} h{Hq}/1")
+
+
+COMPACT_CASES = [(4, 2, 256), (14, 2, 16)]  # (Hq, Hkv, block size): VALU kernel, MFMA kernel
+
+
+@pytest.mark.parametrize("Hq,Hkv,BS", COMPACT_CASES, ids=[f"h{a}-{b}_bs{c}" for a, b, c in COMPACT_CASES])
+def test_decode_compact_list_matches_index_order(Hq, Hkv, BS):
+    """Batches of up to 256 sequences take their splits from a compacted list, larger batches
+    in index order: 256 sequences, and the same 256 plus one padded row (257, index order),
+    give bit-identical outputs, plain and fused; the padded row is zero; both match the oracle."""
+    dev = device()
+    rng = np.random.default_rng(5150 + Hq)
+    ctx = [0, 1, 255, 256, 257, 2048] + [int(x) for x in rng.integers(0, 2048, 250, endpoint=True)]
+    c = decode_case(5150 + Hq, ctx, Hq, Hkv, 128, BS, nb_factor=1.2,
+                    max_blocks_per_seq=2048 // BS)
+    d = DecodeOnDevice(c, dev)
+    say(f"[decode-compact] h={Hq}/{Hkv} bs={BS} B=256 vs 257")
+    D, MBS = c.head_dim, c.max_blocks_per_seq
+
+    def grow(t, fill):
+        pad = torch.full((1,) + tuple(t.shape[1:]), fill, dtype=t.dtype, device=dev)
+        return torch.cat([t, pad]).contiguous()
+
+    q2, tables2, ctx2 = grow(d.q, 0), grow(d.tables, -1), grow(d.ctx, 0)
+    kn2, vn2, slots2 = grow(d.k_new, 0), grow(d.v_new, 0), grow(d.slots, -1)
+    d.store()
+    outs = {}
+    for B, (q, tables, lens) in ((256, (d.q, d.tables, d.ctx)), (257, (q2, tables2, ctx2))):
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+        pa.paged_decode(q, d.k_cache, d.v_cache, tables, lens, c.scale, out)
+        outs[B] = out
+    assert torch.equal(outs[256], outs[257][:256])
+    assert torch.count_nonzero(outs[257][256]).item() == 0
+    kc, vc = oracle.kvcache_store(c.k_new, c.v_new, c.slot_mapping, c.k_cache, c.v_cache)
+    ref = oracle.paged_decode(c.q, kc, vc, c.block_tables, c.context_lens, np.float32(c.scale))
+    err = np.abs(as_f64(outs[256]) - ref).max()
+    say(f"[decode-compact] h={Hq}/{Hkv} bs={BS}: max|err| {err:.3e}")
+    assert err <= ATOL
+    # the fused call, on caches that already hold the new rows (same slots, same values)
+    fused = {}
+    for B, args in ((256, (d.q, d.k_new, d.v_new, d.slots, d.tables, d.ctx)),
+                    (257, (q2, kn2, vn2, slots2, tables2, ctx2))):
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+        qq, kk, vv, ss, tt, ll = args
+        pa.paged_decode_append(qq, kk, vv, ss, d.k_cache, d.v_cache, tt, ll, c.scale, out)
+        fused[B] = out
+    assert torch.equal(fused[256], fused[257][:256])
+    assert np.abs(as_f64(fused[256]) - ref).max() <= ATOL

@@ -163,7 +163,11 @@ int pa_decode_graph_create(int max_batch, int num_q_heads, int num_kv_heads, int
             hipMalloc((void**)&g->meta, metab) == hipSuccess;
   for (int i = 0; ok && i < pa_decode_graph::kStaging; ++i)
     ok = hipHostMalloc((void**)&g->staging[i], metab, hipHostMallocDefault) == hipSuccess &&
-         hipEventCreateWithFlags(&g->uploaded[i], hipEventDisableTiming) == hipSuccess;
+         // the host only needs the copy out of this staging area to have run, not
+         // device memory made visible to it: no system-scope fence at the record
+         // (which would write back and invalidate L2 and stall the stream ~5 us)
+         hipEventCreateWithFlags(&g->uploaded[i],
+                                 hipEventDisableTiming | hipEventDisableSystemFence) == hipSuccess;
   // Zero inputs and sentinel index rows (for the largest packing; a smaller
   // bucket's packing is rewritten by every step that uses it).
   if (ok) {

@@ -367,8 +367,10 @@ int pa_paged_attention_mixed(const void* q, const void* k_new, const void* v_new
   hipStream_t ds = decode_stream ? (hipStream_t)decode_stream : s;
   hipEvent_t fork = nullptr, join = nullptr;
   if (num_decode_seqs > 0 && ds != s) {
-    if (hipEventCreateWithFlags(&fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&join, hipEventDisableTiming) != hipSuccess ||
+    // both streams are on this device: a device-scope release orders them
+    const unsigned ef = hipEventDisableTiming | hipEventReleaseToDevice;
+    if (hipEventCreateWithFlags(&fork, ef) != hipSuccess ||
+        hipEventCreateWithFlags(&join, ef) != hipSuccess ||
         hipEventRecord(fork, s) != hipSuccess || hipStreamWaitEvent(ds, fork, 0) != hipSuccess) {
       if (fork) (void)hipEventDestroy(fork);
       if (join) (void)hipEventDestroy(join);

@@ -1,6 +1,6 @@
-// Streaming-read probe: the device's practical read bandwidth, against which
-// the bandwidth-bound decode kernels are judged (the spec peak is never
-// reached by a real read stream).  Every 16-byte word of the source is loaded
+// Streaming-read probe: the device's practical read bandwidth, the ceiling
+// next to which the bandwidth-bound decode kernels are measured (the spec
+// peak is never reached by a real read stream).  Every 16-byte word of the source is loaded
 // exactly once, eight independent loads in flight per thread.  The loads are
 // non-temporal: for a pure contiguous stream they run about 10% faster than
 // plain loads (6.6-6.9 against 6.0-6.3 TB/s over 512 MiB), so the probe gives

@@ -732,7 +732,7 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int head_dim, int block_size, int
   // the end of a small grid ragged).
   const int64_t half = (p.nsplit_short + 1) / 2;
   p.long_splits = !p.mfma && block_size >= S && p.nsplit_short >= kLongSplitMinShort &&
-                  units * half >= kLongSplitMinGrid;
+                  units * half >= (kv8 ? kLongSplitMinGridFp8 : kLongSplitMinGrid);
   p.nsplit_max = p.long_splits ? (int)half : p.nsplit_short;
   p.compact = B <= kCompactMaxSeqs;
   const int64_t parts = units * p.nsplit_max * p.gt;

@@ -18,8 +18,11 @@ constexpr int kDecodeMaxSplits = 256;
 // spans at least this many short splits ...
 constexpr int kLongSplitMinShort = 8;
 // ... and the grid with half the slots per sequence still has this many
-// workgroups (32 per compute unit of a 256-CU device).
+// workgroups (32 per compute unit of a 256-CU device; 4 on FP8 pools, whose
+// workgroups carry more vector work per byte, so halving their number pays
+// from smaller grids).
 constexpr int64_t kLongSplitMinGrid = 8192;
+constexpr int64_t kLongSplitMinGridFp8 = 1024;
 // Decode grids of up to this many sequences take their (sequence, split)
 // items from a compacted list (4 sequences per lane of one wave in the
 // lookup); larger batches keep index order, where the lookup's extra round

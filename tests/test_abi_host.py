@@ -186,16 +186,18 @@ def test_decode_fp8_argument_checks(lib):
 
 
 def test_decode_fp8_workspace_sizes():
-    # Same split length as bf16 (256 tokens at head_dim 128); at most 4 query heads share a
-    # workgroup, so a group of 8 becomes two sub-groups of 4 with the same partial count.
-    assert pa.decode_fp8_workspace_bytes(64, 16, 8, 128, 256, 16) == \
-        pa.decode_workspace_bytes(64, 16, 8, 128, 256, 16)
+    def ws(parts):  # (max, sum) pairs then 128-float outputs, each region rounded up to 256 B
+        return -(-parts * 8 // 256) * 256 + -(-parts * 512 // 256) * 256
+    # Same short split length as bf16 (256 tokens at head_dim 128), but FP8 pools take long
+    # splits from grids of 1024 workgroups (bf16: 8192): 64 sequences x 8 KV heads with 16
+    # short slots get 8 long ones, twice as long, where bf16 keeps 16.
+    assert pa.decode_fp8_workspace_bytes(64, 16, 8, 128, 256, 16) == ws(64 * 8 * 8 * 2)
+    assert pa.decode_workspace_bytes(64, 16, 8, 128, 256, 16) == ws(64 * 8 * 16 * 2)
+    # 8 heads per KV head run the MFMA kernel on both pools (no long splits there)
     assert pa.decode_fp8_workspace_bytes(64, 64, 8, 128, 16, 64) == \
         pa.decode_workspace_bytes(64, 64, 8, 128, 16, 64)
     # a group of 5 runs the MFMA kernel (bf16 and FP8): one workgroup of 5 heads; a group of 2
     # on FP8 runs the VALU kernel, and 20 heads per KV head the MFMA kernel as two of 10
-    def ws(parts):  # (max, sum) pairs then 128-float outputs, each region rounded up to 256 B
-        return -(-parts * 8 // 256) * 256 + -(-parts * 512 // 256) * 256
     assert pa.decode_workspace_bytes(1, 5, 1, 128, 256, 16) == ws(16 * 5)
     assert pa.decode_fp8_workspace_bytes(1, 5, 1, 128, 256, 16) == ws(16 * 5)
     assert pa.decode_fp8_workspace_bytes(1, 2, 1, 128, 256, 16) == ws(16 * 2)

@@ -464,17 +464,22 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
 // Production tiling: 2 chunks of 32 keys per wave (a split is 256 tokens),
 // both in flight.
 constexpr int kNch = 2;
+// Chunks in flight per wave: both for bf16 pools; one for FP8 pools, whose
+// widening work per chunk already hides the load latency (7B-shaped FP8
+// decode: 292-298 -> 279-281 us; bf16 is level or slower with one).
 constexpr int kDepth = 2;
+constexpr int kDepthFp8 = 1;
 
 template <int D, bool KV8, bool APPEND>
 int launch_mfma_d(const DecodeArgs& a, int B, hipStream_t stream) {
   const unsigned nwg = (unsigned)((int64_t)B * a.hg * a.nsplit_max);
   constexpr int S = kW * kNch * kCK;
+  constexpr int DEPTH = KV8 ? kDepthFp8 : kDepth;
   if ((1 << a.bs_log2) >= S)
-    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, kNch, kDepth, KV8, APPEND, true>), dim3(nwg),
+    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, kNch, DEPTH, KV8, APPEND, true>), dim3(nwg),
                        dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, kNch, kDepth, KV8, APPEND, false>), dim3(nwg),
+    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, kNch, DEPTH, KV8, APPEND, false>), dim3(nwg),
                        dim3(256), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return -1;
   const int gt = (a.group + a.nsub - 1) / a.nsub;

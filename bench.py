@@ -165,8 +165,19 @@ def cpu_baseline(c, kc, vc, budget_s):
         kv += int(c.context_lens[i]) * 2 * c.num_kv_heads * c.head_dim * 2
         tokens += int(c.context_lens[i])
         done += 1
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
     return {"value": round(kv / t_used / 1e9, 4), "unit": "GB/s", "cores": int(cores),
-            "kind": "oracle", "sequences_per_s": round(done / t_used, 2),
+            "kind": "oracle", "cpu_model": cpu_model,
+            "affinity_cores": len(os.sched_getaffinity(0)),
+            "sequences_per_s": round(done / t_used, 2),
             "sample": f"{done} sequence decodes of the 64-sequence decode workload, taken in "
                       f"order with wrap-around ({tokens} context tokens), {t_used:.1f} s of oracle time"}
 

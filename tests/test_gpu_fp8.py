@@ -292,3 +292,23 @@ def test_decode_fp8_long_splits():
     err = np.abs(as_f64(out) - ref).max()
     say(f"[fp8-long] fused store: max|err| {err:.3e}")
     assert err <= ATOL
+
+
+FP8_MAX_CASES = [(2, 1), (7, 1)]  # VALU (long splits: 8 sequences x 128 slots), MFMA
+
+
+@pytest.mark.parametrize("Hq,Hkv", FP8_MAX_CASES, ids=[f"h{a}-{b}" for a, b in FP8_MAX_CASES])
+def test_decode_fp8_max_context(Hq, Hkv):
+    """FP8 pools at the longest context one decode call takes (256 short splits of 256 tokens
+    at head_dim 128, a table exactly that wide), next to one-token and short contexts.  On
+    the VALU kernel 8 sequences make the grid large enough for splits of twice the length."""
+    dev = device()
+    maxc, BS = 256 * 256, 256
+    ctx = [maxc, 1, maxc - 1, 300] + ([4097, 0, 513, 2] if Hq == 2 else [])
+    c = decode_case(9200 + Hq + Hkv, ctx, Hq, Hkv, 128, BS, nb_factor=1.05,
+                    max_blocks_per_seq=maxc // BS)
+    if Hq == 2:  # 8 sequences x 128 long-split slots x 2 heads: long splits are on
+        assert pa.decode_fp8_workspace_bytes(8, 2, 1, 128, BS, maxc // BS) == \
+            -(-8 * 128 * 2 * 8 // 256) * 256 + -(-8 * 128 * 2 * 512 // 256) * 256
+    say(f"[fp8-max] h={Hq}/{Hkv} ctx={ctx}")
+    check_decode(Fp8Pool(c, dev, 0.0125, 0.02), label=f"max context h{Hq}/{Hkv}")

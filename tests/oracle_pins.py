@@ -386,6 +386,27 @@ def pin_e4m3_saturates():
     assert (e4m3_encode(np.array([np.nan]))[0] & 0x7F) == 0x7F
 
 
+def pin_fp8_quantize_matches_torch_every_bf16():
+    """Every bf16 pattern (NaNs of both signs, subnormals, signed zeros) at scales that are not
+    powers of two: the code equals torch's float32 division followed by its float8_e4m3fn cast
+    (round to nearest even, NaN keeps its sign).  Quotients beyond 448 are left out: torch
+    turns them into NaN, where the quantizer saturates (pinned literally above)."""
+    from oracle import quantize
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    x32 = torch.from_numpy((bits.astype(np.uint32) << 16).view(np.float32))
+    for s in (0.3, 0.017, 0.0107, 0.7, 1.0 / 64, 1.7):
+        q32 = x32 / torch.tensor(s, dtype=torch.float32)
+        ref = q32.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        keep = (torch.isnan(q32) | (q32.abs() <= 448.0)).numpy()
+        with np.errstate(over="ignore", invalid="ignore"):
+            got = quantize(bits, s)
+        bad = np.nonzero((got != ref) & keep)[0]
+        assert bad.size == 0, f"scale {s}: {bad.size} codes differ, first bf16 0x{bits[bad[0]]:04x}"
+    # both NaN signs are among the patterns compared
+    nan_codes = quantize(np.array([0x7FC0, 0xFFC0, 0x7F81, 0xFF81], np.uint16), 0.3)
+    assert nan_codes.tolist() == [0x7F, 0xFF, 0x7F, 0xFF]
+
+
 def pin_fp8_quantize_power_of_two_scale():
     """Dividing by 2^k before rounding equals rounding the exponent-shifted value."""
     from oracle import e4m3_encode, quantize

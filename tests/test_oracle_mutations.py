@@ -98,6 +98,17 @@ def _encode_truncate(x):
     lo = np.clip(np.searchsorted(vals, np.minimum(a, 448.0), side="right") - 1, 0, 0x7E)
     return (lo.astype(np.uint8) | (np.signbit(x).astype(np.uint8) << 7)).astype(np.uint8)
 
+def _encode_nan_unsigned(x):
+    x = np.asarray(x, dtype=np.float64)
+    code = ORIGINAL_ENCODE(x)
+    return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
+
+
+def _quantize_f64_division(bits_bf16, scale):
+    x = (np.asarray(bits_bf16, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    return fp8_oracle.e4m3_encode(x.astype(np.float64) / np.float64(np.float32(scale)))
+
+
 ORIGINAL_PREFILL_FP8 = fp8_oracle.paged_prefill_fp8
 
 
@@ -195,7 +206,9 @@ MUTATIONS = {
     "e4m3_ties_away": ("e4m3_encode", _encode_ties_away),
     "e4m3_no_saturation": ("e4m3_encode", _encode_no_saturation),
     "e4m3_truncates": ("e4m3_encode", _encode_truncate),
-    "e4m3_bias_8": ("e4m3_decode", lambda c: fp8_oracle.E4M3_TABLE[np.asarray(c, np.uint8)] / 2.0),
+    "e4m3_nan_loses_sign": ("e4m3_encode", _encode_nan_unsigned),
+    "fp8_quant_divides_in_float64": ("quantize", _quantize_f64_division),
+    "e4m3_bias_8":("e4m3_decode", lambda c: fp8_oracle.E4M3_TABLE[np.asarray(c, np.uint8)] / 2.0),
     "fp8_dequant_ignores_scale": ("dequantize", lambda c, s: fp8_oracle.e4m3_decode(c)),
     "fp8_quant_multiplies": ("quantize", lambda b, s: fp8_oracle.e4m3_encode(
         oracle.bf16_to_f64(b) * np.float32(s))),

@@ -30,8 +30,14 @@ def as_f64(t) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
 
 
+#: Every line the GPU tests printed, for the end-of-run parity summary.
+REPORT = []
+
+
 def say(*msg):
-    print(*msg, flush=True)
+    line = " ".join(str(m) for m in msg)
+    REPORT.append(line)
+    print(line, flush=True)
     sys.stdout.flush()
 
 

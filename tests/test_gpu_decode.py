@@ -28,21 +28,13 @@ def oracle_store(cfg_id):
     return oracle.kvcache_store(c.k_new, c.v_new, c.slot_mapping, c.k_cache, c.v_cache)
 
 
-def sample_rows(c, limit):
-    """Sequences to check against the oracle one by one: extremes, shared members, random."""
-    B = c.batch
-    if B <= limit:
-        return list(range(B))
-    ctx = c.context_lens
-    pick = {int(np.argmin(ctx)), int(np.argmax(ctx))}
-    for g in c.shared_groups[:3]:
-        pick.update(g[:2])
-    rng = np.random.default_rng(99)
-    for i in rng.permutation(B):
-        if len(pick) >= limit:
-            break
-        pick.add(int(i))
-    return sorted(pick)
+@functools.lru_cache(maxsize=None)
+def oracle_decode(cfg_id):
+    """The oracle's outputs for every sequence of a workload (after its store)."""
+    c = workload(cfg_id)
+    kc, vc = oracle_store(cfg_id)
+    say(f"[oracle] workload {cfg_id}: all {c.batch} sequences")
+    return oracle.paged_decode(c.q, kc, vc, c.block_tables, c.context_lens, np.float32(c.scale))
 
 
 @pytest.mark.parametrize("cfg_id", [1, 2, 3, 4])
@@ -77,8 +69,8 @@ def test_gather_bit_exact(cfg_id):
             assert np.array_equal(got[cu[i]:cu[i + 1]], want), (name, i)
 
 
-@pytest.mark.parametrize("cfg_id,limit", [(1, 4), (2, 64), (3, 24), (4, 48)])
-def test_decode_workload(cfg_id, limit):
+@pytest.mark.parametrize("cfg_id", [1, 2, 3, 4])
+def test_decode_workload(cfg_id):
     """Store + decode in the launch configuration the benchmark times; fp32 and bf16 outputs."""
     dev = device()
     c = workload(cfg_id)
@@ -87,13 +79,11 @@ def test_decode_workload(cfg_id, limit):
     d.store()
     out32 = as_f64(d.decode(torch.float32))
     out16 = as_f64(d.decode(torch.bfloat16))
-    kc, vc = oracle_store(cfg_id)
-    rows = sample_rows(c, limit)
-    ref = oracle.paged_decode(c.q[rows], kc, vc, c.block_tables[rows], c.context_lens[rows],
-                              np.float32(c.scale))
-    err32 = np.abs(out32[rows] - ref).max()
-    err16 = np.abs(out16[rows] - ref).max()
-    say(f"[decode] workload {cfg_id}: max|err| fp32 {err32:.3e} bf16 {err16:.3e} over {len(rows)} seqs")
+    ref = oracle_decode(cfg_id)
+    err32 = np.abs(out32 - ref).max()
+    err16 = np.abs(out16 - ref).max()
+    say(f"[decode] workload {cfg_id}: max|err| fp32 {err32:.3e} bf16 {err16:.3e} over all "
+        f"{c.batch} seqs")
     assert err32 <= ATOL and err16 <= ATOL
     assert np.all(np.isfinite(out32))
 
@@ -206,8 +196,9 @@ def test_decode_workspace_shared_by_different_shapes():
         assert np.abs(got - ref).max() <= ATOL
 
 
-def check_append(c, dev, label, rows=None):
-    """Fused store + decode: caches as after the store (bit-exact), outputs within ATOL."""
+def check_append(c, dev, label, ref=None):
+    """Fused store + decode: caches as after the store (bit-exact), outputs of every sequence
+    within ATOL (``ref``: the oracle's outputs when already computed)."""
     d = DecodeOnDevice(c, dev)
     outs = {}
     for dt in (torch.float32, torch.bfloat16):
@@ -218,21 +209,21 @@ def check_append(c, dev, label, rows=None):
         outs[dt] = as_f64(out)
     kc, vc = oracle.kvcache_store(c.k_new, c.v_new, c.slot_mapping, c.k_cache, c.v_cache)
     assert np.array_equal(bits(d.k_cache), kc) and np.array_equal(bits(d.v_cache), vc)
-    rows = list(range(c.batch)) if rows is None else rows
-    ref = oracle.paged_decode(c.q[rows], kc, vc, c.block_tables[rows], c.context_lens[rows],
-                              np.float32(c.scale))
-    e32 = np.abs(outs[torch.float32][rows] - ref).max()
-    e16 = np.abs(outs[torch.bfloat16][rows] - ref).max()
-    say(f"[append] {label}: max|err| fp32 {e32:.3e} bf16 {e16:.3e} over {len(rows)} seqs")
+    if ref is None:
+        ref = oracle.paged_decode(c.q, kc, vc, c.block_tables, c.context_lens,
+                                  np.float32(c.scale))
+    e32 = np.abs(outs[torch.float32] - ref).max()
+    e16 = np.abs(outs[torch.bfloat16] - ref).max()
+    say(f"[append] {label}: max|err| fp32 {e32:.3e} bf16 {e16:.3e} over all {c.batch} seqs")
     assert e32 <= ATOL and e16 <= ATOL
     return outs[torch.float32]
 
 
-@pytest.mark.parametrize("cfg_id,limit", [(1, 4), (2, 64), (3, 24), (4, 48)])
-def test_decode_append_workload(cfg_id, limit):
+@pytest.mark.parametrize("cfg_id", [1, 2, 3, 4])
+def test_decode_append_workload(cfg_id):
     dev = device()
     c = workload(cfg_id)
-    check_append(c, dev, f"workload {cfg_id}", sample_rows(c, limit))
+    check_append(c, dev, f"workload {cfg_id}", oracle_decode(cfg_id))
 
 
 APPEND_SMALL = SMALL + [(64, 16, 4, 2, [512, 513, 1025, 1, 0])]

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import paged_kv_cache_86_amd as pa
-from gpu_util import as_f64, bf16, device, i32, say
+from gpu_util import as_f64, bf16, bits, device, i32, say
 from workloads import config, prefill_case
 
 pytestmark = pytest.mark.gpu
@@ -48,19 +48,28 @@ def test_prefill_workload():
     say(f"[prefill] workload 5: B={p.batch} Tq={p.total_q} prefixes={p.prefix_lens.tolist()}")
     out32 = as_f64(d.run(torch.float32))
     out16 = as_f64(d.run(torch.bfloat16))
-    seqs = sorted({int(np.argmin(p.prefix_lens)), int(np.argmax(p.prefix_lens)), 3, 11})
-    worst32 = worst16 = 0.0
-    for i in seqs:
-        a, b = int(p.cu_seqlens_q[i]), int(p.cu_seqlens_q[i + 1])
-        ref = oracle.paged_prefill(p.q[a:b], p.k_new[a:b], p.v_new[a:b],
-                                   np.array([0, b - a], np.int32), p.k_cache, p.v_cache,
-                                   p.block_tables[i:i + 1], p.context_lens[i:i + 1],
-                                   np.float32(p.scale))
-        worst32 = max(worst32, float(np.abs(out32[a:b] - ref).max()))
-        worst16 = max(worst16, float(np.abs(out16[a:b] - ref).max()))
-    say(f"[prefill] workload 5: max|err| fp32 {worst32:.3e} bf16 {worst16:.3e} over seqs {seqs}")
-    assert worst32 <= ATOL and worst16 <= ATOL
+    say("[oracle] workload 5: all sequences")
+    ref = oracle.paged_prefill(p.q, p.k_new, p.v_new, p.cu_seqlens_q, p.k_cache, p.v_cache,
+                               p.block_tables, p.context_lens, np.float32(p.scale))
+    err32 = float(np.abs(out32 - ref).max())
+    err16 = float(np.abs(out16 - ref).max())
+    say(f"[prefill] workload 5: max|err| fp32 {err32:.3e} bf16 {err16:.3e} over all {p.batch} "
+        f"seqs ({p.total_q} rows)")
+    assert err32 <= ATOL and err16 <= ATOL
     assert np.all(np.isfinite(out32))
+
+
+def test_prefill_workload_chunk_store_bit_exact():
+    """The store of the workload's 8192 chunk tokens: both whole pools bit for bit."""
+    dev = device()
+    p = workload5()
+    d = PrefillOnDevice(p, dev)
+    say(f"[store] workload 5: T={p.total_q}")
+    pa.kvcache_store(d.k_new, d.v_new, d.slots, d.k_cache, d.v_cache)
+    torch.cuda.synchronize()
+    kc, vc = oracle.kvcache_store(p.k_new, p.v_new, p.slot_mapping, p.k_cache, p.v_cache)
+    assert np.array_equal(bits(d.k_cache), kc)
+    assert np.array_equal(bits(d.v_cache), vc)
 
 
 SMALL = [

@@ -47,34 +47,38 @@ class Fp8PrefillOnDevice:
         return out
 
     def oracle_pools(self, blocks):
-        """The oracle's FP8 pools on the given physical blocks (zero codes elsewhere), chunk stored."""
+        """The oracle's FP8 pools on the given physical blocks (zero codes elsewhere), chunk
+        stored.  ``oracle.quantize`` is elementwise: it is evaluated once on every bf16 pattern
+        and the pools are looked up in that table."""
         p = self.p
+        every = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+        with np.errstate(over="ignore", invalid="ignore"):
+            lut_k, lut_v = oracle.quantize(every, self.ks), oracle.quantize(every, self.vs)
         kc8 = np.zeros(p.k_cache.shape, np.uint8)
         vc8 = np.zeros(p.v_cache.shape, np.uint8)
-        kc8[blocks] = oracle.quantize(p.k_cache[blocks], self.ks)
-        vc8[blocks] = oracle.quantize(p.v_cache[blocks], self.vs)
+        kc8[blocks] = lut_k[p.k_cache[blocks]]
+        vc8[blocks] = lut_v[p.v_cache[blocks]]
         return oracle.kvcache_store_fp8(p.k_new, p.v_new, p.slot_mapping, kc8, vc8, self.ks, self.vs)
 
 
-def check(d, seqs, label):
+def check(d, label):
+    """Every chunk row against the oracle; the codes on every block the tables name are
+    compared bit for bit with the oracle's first."""
     p = d.p
     out32 = as_f64(d.run(torch.float32))
     out16 = as_f64(d.run(torch.bfloat16))
-    blocks = np.unique(p.block_tables[seqs][p.block_tables[seqs] >= 0])
+    blocks = np.unique(p.block_tables[p.block_tables >= 0])
     kc8, vc8 = d.oracle_pools(blocks)
     sel = torch.as_tensor(blocks, dtype=torch.int64, device=d.dev)
     assert np.array_equal(codes(d.k8[sel]), kc8[blocks])
     assert np.array_equal(codes(d.v8[sel]), vc8[blocks])
-    worst32 = worst16 = 0.0
-    for i in seqs:
-        a, b = int(p.cu_seqlens_q[i]), int(p.cu_seqlens_q[i + 1])
-        ref = oracle.paged_prefill_fp8(p.q[a:b], np.array([0, b - a], np.int32), kc8, vc8,
-                                       p.block_tables[i:i + 1], p.context_lens[i:i + 1],
-                                       np.float32(p.scale), d.ks, d.vs)
-        worst32 = max(worst32, float(np.abs(out32[a:b] - ref).max()))
-        worst16 = max(worst16, float(np.abs(out16[a:b] - ref).max()))
-    say(f"[prefill-fp8] {label}: max|err| fp32 {worst32:.3e} bf16 {worst16:.3e} over seqs {seqs}")
-    assert worst32 <= ATOL and worst16 <= ATOL
+    ref = oracle.paged_prefill_fp8(p.q, p.cu_seqlens_q, kc8, vc8, p.block_tables,
+                                   p.context_lens, np.float32(p.scale), d.ks, d.vs)
+    err32 = float(np.abs(out32 - ref).max())
+    err16 = float(np.abs(out16 - ref).max())
+    say(f"[prefill-fp8] {label}: max|err| fp32 {err32:.3e} bf16 {err16:.3e} over all "
+        f"{p.batch} seqs")
+    assert err32 <= ATOL and err16 <= ATOL
     assert np.all(np.isfinite(out32))
     return out32, vc8
 
@@ -88,8 +92,7 @@ def test_prefill_fp8_workload():
     vs = float(np.float32(np.abs(oracle.bf16_to_f64(p.v_new)).max() / oracle.E4M3_MAX))
     say(f"[prefill-fp8] workload 5: k_scale={ks:.4g} v_scale={vs:.4g}")
     d = Fp8PrefillOnDevice(p, dev, ks, vs)
-    seqs = sorted({int(np.argmin(p.prefix_lens)), int(np.argmax(p.prefix_lens)), 3, 11})
-    check(d, seqs, "workload 5")
+    check(d, "workload 5")
 
 
 SMALL = [
@@ -112,7 +115,7 @@ def test_prefill_fp8_small_cases(case):
     p = prefill_case(9753 + D + BS + Hq, P, n, Hq, Hkv, D, BS)
     say(f"[prefill-fp8-small] D={D} BS={BS} Hq={Hq} Hkv={Hkv} P={P} n={n}")
     d = Fp8PrefillOnDevice(p, dev, 0.0125, 0.02)
-    out32, vc8 = check(d, list(range(p.batch)), f"D{D} bs{BS} h{Hq}/{Hkv}")
+    out32, vc8 = check(d, f"D{D} bs{BS} h{Hq}/{Hkv}")
     # a chunk's first token with no prefix sees one key: code(v) * v_scale, exactly
     G = Hq // Hkv
     for i in range(p.batch):

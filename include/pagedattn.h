@@ -20,8 +20,11 @@
  * Common conventions
  * ------------------
  * - Every tensor pointer is a DEVICE pointer to a dense row-major buffer that
- *   the caller owns.  No call allocates, frees or synchronizes; every call is
- *   asynchronous on `stream` (a hipStream_t; NULL = the null stream).
+ *   the caller owns.  No call allocates device memory, frees or synchronizes
+ *   (except pa_decode_graph_create / _destroy, and the two events a
+ *   two-stream pa_paged_attention_mixed creates once per thread and device);
+ *   every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *   stream).
  * - bf16 = IEEE bfloat16 bit patterns; indices are int32.
  * - KV cache layout: K and V are separate pools [num_blocks, block_size,
  *   num_kv_heads, head_dim]; the flat slot s = block_id * block_size + offset
@@ -34,8 +37,10 @@
  * - GQA: query head h reads KV head h / (num_q_heads / num_kv_heads).
  * - Supported: head_dim in {64, 128}; block_size a power of two in [1, 1024];
  *   num_q_heads a multiple of num_kv_heads.  Decode additionally needs
- *   max_blocks_per_seq * block_size <= 65536 tokens at head_dim 128 (131072
- *   at head_dim 64): 256 splits of 256 (512) tokens.
+ *   max_blocks_per_seq * block_size <= 65536 tokens (256 splits of 256
+ *   tokens), or 131072 tokens at head_dim 64 with fewer than 3 query heads
+ *   per KV head (that kernel's splits are 512 tokens); otherwise the decode
+ *   calls return PA_ERR_UNSUPPORTED.
  * - Return value: PA_OK, or a negative pa_status.  Argument errors are found
  *   on the host before anything is launched.  PA_ERR_HIP reports a failed
  *   launch (the HIP error is left for the caller's next HIP call to see).
@@ -87,10 +92,13 @@ int pa_kvcache_store(const void* k, const void* v, const int32_t* slot_mapping, 
 
 /*
  * Bytes of scratch pa_paged_decode needs for these sizes (0 if the sizes are
- * invalid).  The workspace holds split-K partial results (a running max and
- * sum per query head and split, then the unnormalised outputs); it needs no
- * initialisation and keeps nothing between calls.  Calls that may run
- * concurrently need separate workspaces.
+ * invalid): the most that any batch of 1 .. num_seqs sequences with the other
+ * sizes equal needs, so one workspace sized for the largest batch serves
+ * every smaller one (the size never decreases as num_seqs grows).  The
+ * workspace holds split-K partial results (a running max and sum per query
+ * head and split, then the unnormalised outputs); it needs no initialisation
+ * and keeps nothing between calls.  It must be 8-byte aligned.  Calls that
+ * may run concurrently need separate workspaces.
  */
 size_t pa_paged_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
                                        int head_dim, int block_size, int max_blocks_per_seq);
@@ -226,7 +234,7 @@ int pa_paged_prefill_fp8(const void* q, const int32_t* cu_seqlens_q, int num_seq
  * pinned host memory and uploaded with non-blocking copies).
  *
  * An opaque object that owns static device buffers (q, new K/V rows, output,
- * index arrays, split-K workspace), two pinned host staging areas, and one
+ * index arrays, split-K workspace), four pinned host staging areas, and one
  * instantiated HIP graph per bucket of the fused store + decode call
  * (pa_paged_decode_append, or pa_paged_decode_append_fp8 when kv_fp8 != 0)
  * over the caller's caches.  Unlike the other calls, create allocates (device
@@ -248,8 +256,8 @@ int pa_paged_prefill_fp8(const void* q, const int32_t* cu_seqlens_q, int num_seq
  *   [batch, tables_stride] (tables_stride <= max_blocks_per_seq) are HOST
  *   arrays: they are copied into pinned staging (rows batch..bucket-1 get
  *   slot -1, length 0 and table -1) and uploaded asynchronously; the host
- *   blocks only if the staging area it is about to refill is still being
- *   uploaded by the step before last.  out: device pointer that receives the
+ *   blocks only if the staging area it is about to refill (the one used four
+ *   steps earlier) is still being uploaded.  out: device pointer that receives the
  *   batch's rows (NULL = leave them in the static output).  Must be called on
  *   the device the object was created on; consecutive runs of one object
  *   must use the same stream (or be ordered by the caller).
@@ -308,13 +316,20 @@ int pa_paged_prefill(const void* q, const void* k_new, const void* v_new,
  *   workspace: pa_paged_decode_workspace_bytes(num_decode_seqs, ...).
  * Effect: every new token is stored (slot < 0 skips), then each row attends
  * to its sequence's keys 0 .. its position, as pa_paged_prefill would for a
- * q_len-1 chunk and as pa_paged_decode does.  The chunks' tokens are stored
- * before any chunk is attended, so a chunk may read a block another chunk of
- * the same call fills.  The decode rows run as pa_paged_decode_append; with
- * decode_stream != NULL and != stream they run on decode_stream, forked from
- * and joined back into `stream` with events (the call then returns with all
- * of its work ordered before later work on `stream`).  decode_stream must
- * have default priority.
+ * q_len-1 chunk and as pa_paged_decode does.  Every token of the call is
+ * stored before any row that could read it attends, so a chunk may read a
+ * block that another chunk or a decode row of the same call fills (prefix
+ * caching registers a block as soon as its last token arrives).  On one
+ * stream: the chunks' tokens are stored, then the decode rows run as
+ * pa_paged_decode_append (storing their own tokens), then the chunks attend.
+ * With decode_stream != NULL and != stream: every token is stored on
+ * `stream`, then the decode rows run as pa_paged_decode on decode_stream
+ * while the chunks attend on `stream`; decode_stream is forked from and
+ * joined back into `stream` with two events (the call then returns with all
+ * of its work ordered before later work on `stream`).  The events are
+ * created by the first such call on a thread and device and kept until the
+ * process ends (the only objects this call creates).  decode_stream must
+ * have default priority and be on the current device.
  */
 int pa_paged_attention_mixed(const void* q, const void* k_new, const void* v_new,
                              const int32_t* slot_mapping, const int32_t* cu_seqlens_q,

@@ -222,13 +222,14 @@ _workspaces = {}
 
 
 def decode_workspace(nbytes: int, device):
-    """A byte buffer of at least ``nbytes`` for decode partials, kept per device and reused."""
+    """A byte buffer of at least ``nbytes`` for decode partials and arrival counters, kept per
+    device and reused (zeroed when allocated; every decode call leaves its counters at zero)."""
     torch = _torch()
     dev = torch.device(device)
     key = dev.index if dev.index is not None else torch.cuda.current_device()
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
         _workspaces[key] = ws
     return ws
 

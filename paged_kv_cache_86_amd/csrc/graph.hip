@@ -174,7 +174,8 @@ int pa_decode_graph_create(int max_batch, int num_q_heads, int num_kv_heads, int
     stage(g, g->staging[0], 0, max_batch, nullptr, nullptr, 0, nullptr);
     ok = hipMemcpy(g->meta, g->staging[0], metab, hipMemcpyHostToDevice) == hipSuccess &&
          hipMemset(g->q, 0, qb) == hipSuccess && hipMemset(g->k_new, 0, kvb) == hipSuccess &&
-         hipMemset(g->v_new, 0, kvb) == hipSuccess && hipDeviceSynchronize() == hipSuccess;
+         hipMemset(g->v_new, 0, kvb) == hipSuccess && hipMemset(g->workspace, 0, ws) == hipSuccess &&
+         hipDeviceSynchronize() == hipSuccess;
   }
   if (ok) {
     for (int b : {1, 2, 4, 8})

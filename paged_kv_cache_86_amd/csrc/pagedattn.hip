@@ -69,6 +69,12 @@ int pa_kvcache_store(const void* k, const void* v, const int32_t* slot_mapping, 
 
 namespace {
 
+// Workspace of a decode call with num_seqs sequences: the most any batch of
+// 1 .. num_seqs sequences needs, so one workspace serves every smaller batch.
+// A plan's own size grows with the batch except where long splits switch on
+// (half the partial slots per sequence); that happens once, at a threshold
+// batch, so the maximum is the larger of the plan at num_seqs and the plan
+// just below the threshold.
 size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                               int block_size, int max_blocks_per_seq, bool kv8) {
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
@@ -76,10 +82,31 @@ size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, i
     return 0;
   const pa::DecodePlan p = pa::plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                            block_size, max_blocks_per_seq, kv8);
-  return (p.units > pa::kDecodeMaxUnits || p.nsplit_short > pa::kDecodeMaxSplits)
-             ? 0
-             : p.workspace_bytes();
+  if (p.units > pa::kDecodeMaxUnits || p.nsplit_short > pa::kDecodeMaxSplits) return 0;
+  size_t bytes = p.workspace_bytes();
+  if (p.long_splits) {
+    // largest batch below num_seqs whose plan keeps short splits
+    int lo = 1, hi = num_seqs - 1, below = 0;
+    while (lo <= hi) {
+      const int mid = lo + (hi - lo) / 2;
+      if (pa::plan_decode(mid, num_q_heads, num_kv_heads, head_dim, block_size,
+                          max_blocks_per_seq, kv8).long_splits) {
+        hi = mid - 1;
+      } else {
+        below = mid;
+        lo = mid + 1;
+      }
+    }
+    if (below > 0) {
+      const size_t b = pa::plan_decode(below, num_q_heads, num_kv_heads, head_dim, block_size,
+                                       max_blocks_per_seq, kv8).workspace_bytes();
+      if (b > bytes) bytes = b;
+    }
+  }
+  return bytes;
 }
+
+
 
 // The new tokens of a fused store + decode call (all NULL for plain decode).
 struct NewTokens {
@@ -110,7 +137,7 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   if (append && (!append->k || !append->v || !append->slot_mapping)) return PA_ERR_NULL;
   const pa::DecodePlan p = pa::plan_decode(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                            block_size, max_blocks_per_seq, kv8);
-  if (!workspace) return PA_ERR_WORKSPACE;
+  if (!workspace || ((uintptr_t)workspace & 7) != 0) return PA_ERR_WORKSPACE;
   if (workspace_bytes < p.workspace_bytes()) return PA_ERR_WORKSPACE;
   const int64_t hg = (int64_t)num_kv_heads * p.nsub;
   if ((int64_t)num_seqs * hg * p.nsplit_max > INT32_MAX) return PA_ERR_SHAPE;
@@ -250,6 +277,28 @@ int pa_kvcache_store_fp8(const void* k, const void* v, const int32_t* slot_mappi
 
 namespace {
 
+// The fork and join events of two-stream mixed calls: two per thread and
+// device, created by the first such call and kept until the process ends (an
+// event's record and the waits on it are consumed at the call, so a thread
+// reuses its pair).  Device scope: both streams are on the current device.
+int fork_join_events(hipEvent_t* fork, hipEvent_t* join) {
+  constexpr int kMaxDevices = 64;
+  thread_local hipEvent_t events[kMaxDevices][2] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+  for (int i = 0; i < 2; ++i) {
+    if (!events[dev][i] &&
+        hipEventCreateWithFlags(&events[dev][i], hipEventDisableTiming |
+                                                     hipEventReleaseToDevice) != hipSuccess) {
+      events[dev][i] = nullptr;
+      return -1;
+    }
+  }
+  *fork = events[dev][0];
+  *join = events[dev][1];
+  return 0;
+}
+
 // Shared argument checks and launch of both prefill forms (kv8: FP8 pools,
 // every key from the cache; otherwise bf16 pools, the chunk's keys from k_new / v_new).
 int prefill(const void* q, const void* k_new, const void* v_new, const int32_t* cu_seqlens_q,
@@ -357,38 +406,44 @@ int pa_paged_attention_mixed(const void* q, const void* k_new, const void* v_new
     if (need == 0) return PA_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
   }
-  // 1. the chunks' new K/V go into the cache first: a sequence of this step may
-  //    reuse a block another one fills in this step, and reads it from the cache
-  int rc = pa_kvcache_store(k_new, v_new, slot_mapping, prefill_tokens, k_cache, v_cache,
-                            num_blocks, block_size, num_kv_heads, head_dim, stream);
-  if (rc != PA_OK) return rc;
-  // 2. the decode rows, optionally on a second stream that joins back afterwards
   hipStream_t s = (hipStream_t)stream;
   hipStream_t ds = decode_stream ? (hipStream_t)decode_stream : s;
+  const bool two_streams = num_decode_seqs > 0 && ds != s;
+  // 1. new K/V into the cache before anything attends: a sequence of this
+  //    step may reuse a block another one fills in this step, and reads it
+  //    from the cache.  On one stream the decode rows store theirs in their
+  //    fused call, which runs before the chunks; with a second stream every
+  //    row is stored here, before the fork.
+  const int stored = two_streams ? prefill_tokens + num_decode_seqs : prefill_tokens;
+  int rc = pa_kvcache_store(k_new, v_new, slot_mapping, stored, k_cache, v_cache, num_blocks,
+                            block_size, num_kv_heads, head_dim, stream);
+  if (rc != PA_OK) return rc;
+  // 2. the decode rows, optionally on a second stream that joins back afterwards
   hipEvent_t fork = nullptr, join = nullptr;
-  if (num_decode_seqs > 0 && ds != s) {
-    // both streams are on this device: a device-scope release orders them
-    const unsigned ef = hipEventDisableTiming | hipEventReleaseToDevice;
-    if (hipEventCreateWithFlags(&fork, ef) != hipSuccess ||
-        hipEventCreateWithFlags(&join, ef) != hipSuccess ||
-        hipEventRecord(fork, s) != hipSuccess || hipStreamWaitEvent(ds, fork, 0) != hipSuccess) {
-      if (fork) (void)hipEventDestroy(fork);
-      if (join) (void)hipEventDestroy(join);
+  if (two_streams) {
+    if (fork_join_events(&fork, &join) != 0 || hipEventRecord(fork, s) != hipSuccess ||
+        hipStreamWaitEvent(ds, fork, 0) != hipSuccess)
       return PA_ERR_HIP;
-    }
   }
   if (num_decode_seqs > 0) {
     const size_t qrow = (size_t)num_q_heads * head_dim;
     const size_t kvrow = (size_t)num_kv_heads * head_dim;
     const size_t orow = qrow * (out_dtype == PA_F32 ? 4 : 2);
-    rc = pa_paged_decode_append(
-        (const uint16_t*)q + (size_t)prefill_tokens * qrow,
-        (const uint16_t*)k_new + (size_t)prefill_tokens * kvrow,
-        (const uint16_t*)v_new + (size_t)prefill_tokens * kvrow, slot_mapping + prefill_tokens,
-        k_cache, v_cache, block_tables + (size_t)num_prefill_seqs * max_blocks_per_seq,
-        max_blocks_per_seq, context_lens + num_prefill_seqs, num_decode_seqs, num_q_heads,
-        num_kv_heads, head_dim, block_size, num_blocks, scale,
-        (char*)out + (size_t)prefill_tokens * orow, out_dtype, workspace, workspace_bytes, ds);
+    const void* qd = (const uint16_t*)q + (size_t)prefill_tokens * qrow;
+    const int32_t* td = block_tables + (size_t)num_prefill_seqs * max_blocks_per_seq;
+    const int32_t* cd = context_lens + num_prefill_seqs;
+    void* od = (char*)out + (size_t)prefill_tokens * orow;
+    if (two_streams)
+      rc = pa_paged_decode(qd, k_cache, v_cache, td, max_blocks_per_seq, cd, num_decode_seqs,
+                           num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, od,
+                           out_dtype, workspace, workspace_bytes, ds);
+    else
+      rc = pa_paged_decode_append(
+          qd, (const uint16_t*)k_new + (size_t)prefill_tokens * kvrow,
+          (const uint16_t*)v_new + (size_t)prefill_tokens * kvrow, slot_mapping + prefill_tokens,
+          k_cache, v_cache, td, max_blocks_per_seq, cd, num_decode_seqs, num_q_heads,
+          num_kv_heads, head_dim, block_size, num_blocks, scale, od, out_dtype, workspace,
+          workspace_bytes, s);
   }
   // 3. the chunks
   if (rc == PA_OK && num_prefill_seqs > 0 && prefill_tokens > 0)
@@ -397,12 +452,10 @@ int pa_paged_attention_mixed(const void* q, const void* k_new, const void* v_new
                           v_cache, block_tables, max_blocks_per_seq, context_lens, num_q_heads,
                           num_kv_heads, head_dim, block_size, num_blocks, scale, out, out_dtype,
                           stream);
-  if (fork) {
+  if (two_streams) {
     // join even after an error, so the caller's stream never runs ahead of the decode work
     const bool ok = hipEventRecord(join, ds) == hipSuccess &&
                     hipStreamWaitEvent(s, join, 0) == hipSuccess;
-    (void)hipEventDestroy(fork);
-    (void)hipEventDestroy(join);
     if (!ok && rc == PA_OK) rc = PA_ERR_HIP;
   }
   return rc;

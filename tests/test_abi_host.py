@@ -83,20 +83,40 @@ def test_decode_argument_checks(lib):
     assert decode(lib, MBS=4097, BS=16, ws_bytes=1 << 30) == PA_ERR_UNSUPPORTED  # > 65536 tokens
 
 
+def _ws(units, parts, D=128):
+    """Decode workspace layout: per partial (unit, split slot, head) a (max, sum) pair, then
+    D-float unnormalised outputs; each region rounded up to 256 bytes."""
+    r = lambda x: -(-x // 256) * 256  # noqa: E731
+    return r(parts * 8) + r(parts * D * 4)
+
+
 def test_decode_workspace_sizes():
-    # Qwen3-0.6B-shaped decode: 64 x 8 head groups, 16 splits of 256 tokens, 2 heads x (128 + 2) floats
-    b = pa.decode_workspace_bytes(64, 16, 8, 128, 256, 16)
-    assert b == 64 * 8 * 16 * 2 * 2 * 4 + 64 * 8 * 16 * 2 * 128 * 4
+    # Qwen3-0.6B-shaped decode: 64 x 8 head groups, 16 splits of 256 tokens, 2 heads per group
+    assert pa.decode_workspace_bytes(64, 16, 8, 128, 256, 16) == _ws(64 * 8, 64 * 8 * 16 * 2)
     assert pa.decode_workspace_bytes(0, 16, 8, 128, 256, 16) == 0
     # 128 x 8 head groups x 8 slots reach 8192 workgroups: splits of 512 tokens for contexts
-    # above 8 x 256, so 8 partial slots per head group instead of 16
-    assert pa.decode_workspace_bytes(128, 16, 8, 128, 256, 16) == 128 * 8 * 8 * 2 * (2 + 128) * 4
+    # above 8 x 256 (8 partial slots per head group instead of 16); the size is the most any
+    # smaller batch needs, here 127 sequences with short splits
+    assert pa.decode_workspace_bytes(128, 16, 8, 128, 256, 16) == _ws(127 * 8, 127 * 8 * 16 * 2)
     # with blocks smaller than a split the block ids stay in LDS: short splits only
-    assert pa.decode_workspace_bytes(128, 16, 8, 128, 16, 256) == 128 * 8 * 16 * 2 * (2 + 128) * 4
+    assert pa.decode_workspace_bytes(128, 16, 8, 128, 16, 256) == _ws(128 * 8, 128 * 8 * 16 * 2)
     assert pa.decode_workspace_bytes(4, 6, 4, 128, 16, 8) == 0  # 6 % 4 != 0
     assert pa.decode_workspace_bytes(4, 8, 4, 128, 16, 4097) == 0  # context above 65536 tokens
     # more query heads per KV head than one workgroup serves: split into sub-groups
     assert pa.decode_workspace_bytes(2, 32, 2, 64, 16, 4) > pa.decode_workspace_bytes(2, 16, 2, 64, 16, 4)
+
+
+@pytest.mark.parametrize("shape", [(16, 8, 128, 256, 16, False), (16, 8, 128, 256, 16, True),
+                                   (16, 8, 64, 512, 16, False), (2, 1, 128, 256, 256, False),
+                                   (2, 1, 128, 256, 256, True), (28, 4, 128, 16, 512, False)])
+def test_decode_workspace_never_shrinks_with_the_batch(shape):
+    """A workspace sized for a batch serves every smaller batch (long splits, which halve the
+    partial slots, switch on at a threshold batch)."""
+    Hq, Hkv, D, BS, MBS, fp8 = shape
+    f = pa.decode_fp8_workspace_bytes if fp8 else pa.decode_workspace_bytes
+    sizes = [f(b, Hq, Hkv, D, BS, MBS) for b in range(1, 400)]
+    assert all(x > 0 for x in sizes)
+    assert all(a <= b for a, b in zip(sizes, sizes[1:]))
 
 
 def prefill(lib, B=2, Tq=10, mq=5, q=FAKE, D=128, BS=16, Hq=4, Hkv=2):
@@ -186,22 +206,20 @@ def test_decode_fp8_argument_checks(lib):
 
 
 def test_decode_fp8_workspace_sizes():
-    def ws(parts):  # (max, sum) pairs then 128-float outputs, each region rounded up to 256 B
-        return -(-parts * 8 // 256) * 256 + -(-parts * 512 // 256) * 256
     # Same short split length as bf16 (256 tokens at head_dim 128), but FP8 pools take long
     # splits from grids of 1024 workgroups (bf16: 8192): 64 sequences x 8 KV heads with 16
     # short slots get 8 long ones, twice as long, where bf16 keeps 16.
-    assert pa.decode_fp8_workspace_bytes(64, 16, 8, 128, 256, 16) == ws(64 * 8 * 8 * 2)
-    assert pa.decode_workspace_bytes(64, 16, 8, 128, 256, 16) == ws(64 * 8 * 16 * 2)
+    assert pa.decode_fp8_workspace_bytes(64, 16, 8, 128, 256, 16) == _ws(64 * 8, 64 * 8 * 8 * 2)
+    assert pa.decode_workspace_bytes(64, 16, 8, 128, 256, 16) == _ws(64 * 8, 64 * 8 * 16 * 2)
     # 8 heads per KV head run the MFMA kernel on both pools (no long splits there)
     assert pa.decode_fp8_workspace_bytes(64, 64, 8, 128, 16, 64) == \
         pa.decode_workspace_bytes(64, 64, 8, 128, 16, 64)
     # a group of 5 runs the MFMA kernel (bf16 and FP8): one workgroup of 5 heads; a group of 2
     # on FP8 runs the VALU kernel, and 20 heads per KV head the MFMA kernel as two of 10
-    assert pa.decode_workspace_bytes(1, 5, 1, 128, 256, 16) == ws(16 * 5)
-    assert pa.decode_fp8_workspace_bytes(1, 5, 1, 128, 256, 16) == ws(16 * 5)
-    assert pa.decode_fp8_workspace_bytes(1, 2, 1, 128, 256, 16) == ws(16 * 2)
-    assert pa.decode_fp8_workspace_bytes(1, 20, 1, 128, 256, 16) == ws(16 * 20)
+    assert pa.decode_workspace_bytes(1, 5, 1, 128, 256, 16) == _ws(1, 16 * 5)
+    assert pa.decode_fp8_workspace_bytes(1, 5, 1, 128, 256, 16) == _ws(1, 16 * 5)
+    assert pa.decode_fp8_workspace_bytes(1, 2, 1, 128, 256, 16) == _ws(1, 16 * 2)
+    assert pa.decode_fp8_workspace_bytes(1, 20, 1, 128, 256, 16) == _ws(2, 16 * 20)
     assert pa.decode_fp8_workspace_bytes(4, 6, 4, 128, 16, 8) == 0
 
 

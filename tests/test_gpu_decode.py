@@ -263,9 +263,10 @@ def test_decode_long_splits(D, BS):
     oracle, plain and fused store."""
     dev = device()
     c = _long_split_case(4321 + D + BS, D, BS)
-    B, P = c.batch, 8
-    parts = B * 8 * P * 2  # (sequence, KV head) x slots x query heads per workgroup
-    assert pa.decode_workspace_bytes(B, 16, 8, D, BS, c.max_blocks_per_seq) == parts * (2 + D) * 4
+    B = c.batch  # 128 x 8 head groups x 8 long-split slots = 8192 workgroups: long splits on,
+    # so the plan at 128 needs less than 127 sequences with short splits (the size is the most)
+    ws = [pa.decode_workspace_bytes(b, 16, 8, D, BS, c.max_blocks_per_seq) for b in (126, 127, B)]
+    assert ws[0] < ws[1] == ws[2]
     say(f"[decode-long] D={D} BS={BS} B={B} ctx max {int(c.context_lens.max())}")
     d = DecodeOnDevice(c, dev)
     d.store()
@@ -350,3 +351,37 @@ def test_decode_compact_list_matches_index_order(Hq, Hkv, BS):
         fused[B] = out
     assert torch.equal(fused[256], fused[257][:256])
     assert np.abs(as_f64(fused[256]) - ref).max() <= ATOL
+
+
+REUSE_SHAPES = [  # (Hq, Hkv, D, BS, MBS, batch): VALU short / long splits, MFMA
+    (16, 8, 128, 256, 16, 64), (16, 8, 128, 256, 16, 128), (28, 4, 128, 16, 128, 40),
+    (4, 2, 64, 16, 64, 33)]
+
+
+def test_decode_workspace_reuse_matches_fresh_workspace():
+    """The last workgroup of each (sequence, head group) merges the split partials, counting
+    arrivals in the workspace.  One workspace that starts as garbage and is reused by calls of
+    different shapes and data, back to back on the stream, gives bit-identical outputs to
+    calls on freshly zeroed workspaces (no stale partial or count is ever read)."""
+    dev = device()
+    rng = np.random.default_rng(4242)
+    nbytes = max(pa.decode_workspace_bytes(B, Hq, Hkv, D, BS, MBS)
+                 for Hq, Hkv, D, BS, MBS, B in REUSE_SHAPES)
+    shared = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device=dev)
+    runs = []
+    for it in range(12):
+        Hq, Hkv, D, BS, MBS, B = REUSE_SHAPES[it % len(REUSE_SHAPES)]
+        ctx = rng.integers(0, MBS * BS, size=B, endpoint=True)
+        c = decode_case(7000 + it, ctx, Hq, Hkv, D, BS, nb_factor=1.2, max_blocks_per_seq=MBS)
+        d = DecodeOnDevice(c, dev)
+        d.store()
+        runs.append((c, d, d.decode(torch.float32, workspace=shared)))  # no sync between calls
+    torch.cuda.synchronize()
+    say(f"[decode-reuse] {len(runs)} calls on one workspace of {nbytes} bytes")
+    for c, d, got in runs:
+        fresh = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        assert torch.equal(got, d.decode(torch.float32, workspace=fresh))
+    c, d, got = runs[2]
+    kc, vc = oracle.kvcache_store(c.k_new, c.v_new, c.slot_mapping, c.k_cache, c.v_cache)
+    ref = oracle.paged_decode(c.q, kc, vc, c.block_tables, c.context_lens, np.float32(c.scale))
+    assert np.abs(as_f64(got) - ref).max() <= ATOL

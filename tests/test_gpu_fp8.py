@@ -281,7 +281,6 @@ def test_decode_fp8_long_splits():
     rng = np.random.default_rng(4444)
     ctx = edges + [int(x) for x in rng.integers(1, 16 * S, 128 - len(edges), endpoint=True)]
     c = decode_case(4444, ctx, 16, 8, 128, 256, nb_factor=1.2, max_blocks_per_seq=16)
-    assert pa.decode_fp8_workspace_bytes(128, 16, 8, 128, 256, 16) == 128 * 8 * 8 * 2 * 130 * 4
     say(f"[fp8-long] B=128 ctx max {int(c.context_lens.max())}")
     check_decode(Fp8Pool(c, dev, 0.0125, 0.02), label="long splits")
     ks, vs = 0.0125, 0.02
@@ -320,8 +319,9 @@ def test_decode_fp8_max_context(Hq, Hkv):
     ctx = [maxc, 1, maxc - 1, 300] + ([4097, 0, 513, 2] if Hq == 2 else [])
     c = decode_case(9200 + Hq + Hkv, ctx, Hq, Hkv, 128, BS, nb_factor=1.05,
                     max_blocks_per_seq=maxc // BS)
-    if Hq == 2:  # 8 sequences x 128 long-split slots x 2 heads: long splits are on
-        assert pa.decode_fp8_workspace_bytes(8, 2, 1, 128, BS, maxc // BS) == \
-            -(-8 * 128 * 2 * 8 // 256) * 256 + -(-8 * 128 * 2 * 512 // 256) * 256
+    if Hq == 2:  # 8 sequences x 128 long-split slots: long splits are on, so the plan at 8
+        # needs less than 7 sequences with short splits (the size is the most of either)
+        ws = [pa.decode_fp8_workspace_bytes(b, 2, 1, 128, BS, maxc // BS) for b in (6, 7, 8)]
+        assert ws[0] < ws[1] == ws[2]
     say(f"[fp8-max] h={Hq}/{Hkv} ctx={ctx}")
     check_decode(Fp8Pool(c, dev, 0.0125, 0.02), label=f"max context h{Hq}/{Hkv}")

@@ -129,3 +129,29 @@ def test_graph_fp8_cache():
         assert torch.equal(o, e)
         assert torch.equal(kg, ke) and torch.equal(vg, ve)
     g.close()
+
+
+def test_graph_max_batch_across_long_split_threshold():
+    """max_batch 128 at 16/8 heads, block 256: long splits switch on at 128 sequences, and the
+    bucket of 112 needs more workspace than the plan at 128; every bucket's capture and replay
+    works and equals the eager call."""
+    dev = device()
+    rng = np.random.default_rng(505)
+    ctx = rng.integers(1, 4097, size=128)
+    c = decode_case(505, ctx, 16, 8, 128, 256, nb_factor=1.2, max_blocks_per_seq=16)
+    kc_g, vc_g = bf16(c.k_cache, dev), bf16(c.v_cache, dev)
+    kc_e, vc_e = bf16(c.k_cache, dev), bf16(c.v_cache, dev)
+    g = pa.DecodeGraph(kc_g, vc_g, 128, c.num_q_heads, c.max_blocks_per_seq, c.scale,
+                       out_dtype=torch.float32)
+    for B in (112, 128, 100):
+        rows = np.arange(B)
+        say(f"[graph-128] batch {B} -> bucket {g.bucket(B)}")
+        o = torch.empty((B, c.num_q_heads, c.head_dim), dtype=torch.float32, device=dev)
+        g.run(B, bf16(c.q[rows], dev), bf16(c.k_new[rows], dev), bf16(c.v_new[rows], dev),
+              c.slot_mapping[rows], c.block_tables[rows], c.context_lens[rows], out=o)
+        torch.cuda.synchronize()
+        e = eager_step(c, rows, kc_e, vc_e, dev, torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(o, e)
+        assert same_bits(kc_g, kc_e) and same_bits(vc_g, vc_e)
+    g.close()

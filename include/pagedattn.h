@@ -69,7 +69,8 @@ typedef enum {
   PA_ERR_WORKSPACE = -4,   /* decode workspace missing or too small */
   PA_ERR_HIP = -5,         /* a kernel launch (or another HIP call) failed */
   PA_ERR_OUT_OF_BLOCKS = -6, /* block manager: not enough free blocks */
-  PA_ERR_SEQUENCE = -7     /* block manager: unknown (or already allocated) sequence id */
+  PA_ERR_SEQUENCE = -7,    /* block manager: unknown (or already allocated) sequence id */
+  PA_ERR_SCRATCH = -8      /* the call needs more than the library's fixed scratch buffer */
 } pa_status;
 
 typedef enum { PA_BF16 = 0, PA_F32 = 1 } pa_dtype; /* output element type */
@@ -148,6 +149,29 @@ int pa_paged_decode_append(const void* q, const void* k_new, const void* v_new,
                            int num_kv_heads, int head_dim, int block_size, int num_blocks,
                            float scale, void* out, int out_dtype, void* workspace,
                            size_t workspace_bytes, void* stream);
+
+/*
+ * Fused store + decode without a caller workspace, for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same operation, arguments and kernels as
+ * pa_paged_decode_append, with the split-K partials in a scratch array the
+ * library holds in device memory (PA_DECODE_SCRATCH_BYTES per GPU, from the
+ * first such call on that GPU until the process ends).  The call allocates and
+ * frees nothing.  Sizes whose pa_paged_decode_workspace_bytes exceeds
+ * PA_DECODE_SCRATCH_BYTES return PA_ERR_SCRATCH (before anything is launched).
+ * Every call on one GPU uses that GPU's one array, so calls that may overlap
+ * in time on one GPU (other streams, other threads) race and give wrong
+ * results; calls ordered on one stream are safe.  The scratch needs no
+ * clearing between calls.
+ */
+#define PA_DECODE_SCRATCH_BYTES ((size_t)64 << 20)
+int pa_paged_decode_append_noalloc(const void* q, const void* k_new, const void* v_new,
+                                   const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                                   const int32_t* block_tables, int max_blocks_per_seq,
+                                   const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                   int num_kv_heads, int head_dim, int block_size,
+                                   int num_blocks, float scale, void* out, int out_dtype,
+                                   void* stream);
 
 /*
  * FP8 KV cache (VLLM 0.7.3 source article §5.3, KV cache precision: the cache

@@ -21,6 +21,9 @@ LIB_PATH = os.path.join(HERE, "libpagedattn.so")
 PA_OK = 0
 PA_BF16 = 0
 PA_F32 = 1
+PA_ERR_SCRATCH = -8
+#: Bytes of the fixed scratch array pa_paged_decode_append_noalloc uses on each GPU.
+DECODE_SCRATCH_BYTES = 64 << 20
 
 #: Every symbol ``include/pagedattn.h`` declares.
 EXPORTED_SYMBOLS = (
@@ -37,6 +40,7 @@ EXPORTED_SYMBOLS = (
     "pa_paged_decode_fp8",
     "pa_paged_decode_append",
     "pa_paged_decode_append_fp8",
+    "pa_paged_decode_append_noalloc",
     "pa_decode_graph_create",
     "pa_decode_graph_buffers",
     "pa_decode_graph_bucket",
@@ -109,6 +113,9 @@ def load_library() -> ctypes.CDLL:
     lib.pa_paged_decode_append_fp8.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, F,
                                                F, F, P, I, P, Z, P]
     lib.pa_paged_decode_append_fp8.restype = I
+    lib.pa_paged_decode_append_noalloc.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, F,
+                                                   P, I, P]
+    lib.pa_paged_decode_append_noalloc.restype = I
     PP = ctypes.POINTER(ctypes.c_void_p)
     lib.pa_decode_graph_create.argtypes = [I, I, I, I, I, I, I, I, F, F, F, P, P, I, PP]
     lib.pa_decode_graph_create.restype = I
@@ -297,6 +304,21 @@ def paged_decode_append(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_t
         _ptr(block_tables), MBS, _ptr(context_lens), B, Hq, Hkv, D, BS, NB, sc, _ptr(out),
         _out_dtype(out), _ptr(workspace), int(workspace.numel()), _stream(q.device))
     _raise_on("pa_paged_decode_append", rc)
+
+
+def paged_decode_append_noalloc(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
+                                context_lens, scale: Optional[float], out) -> None:
+    """paged_decode_append with the library's fixed per-GPU scratch instead of a workspace: no
+    device memory is allocated by this call or by the library behind it."""
+    NB, BS, Hkv, D = _cache_geometry(k_cache, v_cache)
+    B, Hq, MBS = _decode_shapes(q, block_tables, context_lens, out, D)
+    _new_tokens(k_new, v_new, slot_mapping, B, Hkv, D)
+    sc = float(scale) if scale is not None else 0.0
+    rc = load_library().pa_paged_decode_append_noalloc(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache),
+        _ptr(block_tables), MBS, _ptr(context_lens), B, Hq, Hkv, D, BS, NB, sc, _ptr(out),
+        _out_dtype(out), _stream(q.device))
+    _raise_on("pa_paged_decode_append_noalloc", rc)
 
 
 def kvcache_store_fp8(k, v, slot_mapping, k_cache, v_cache, k_scale: float,

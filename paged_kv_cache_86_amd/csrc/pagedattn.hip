@@ -4,6 +4,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "kernels.h"
 
 namespace {
@@ -45,6 +47,9 @@ const char* pa_status_string(int status) {
     case PA_ERR_HIP: return "PA_ERR_HIP: kernel launch or HIP call failed";
     case PA_ERR_OUT_OF_BLOCKS: return "PA_ERR_OUT_OF_BLOCKS: not enough free KV blocks";
     case PA_ERR_SEQUENCE: return "PA_ERR_SEQUENCE: unknown or already allocated sequence";
+    case PA_ERR_SCRATCH:
+      return "PA_ERR_SCRATCH: the decode needs more than the library's fixed scratch buffer "
+             "(PA_DECODE_SCRATCH_BYTES); pass a workspace to pa_paged_decode_append instead";
     default: return "unknown pa_status";
   }
 }
@@ -237,6 +242,63 @@ int pa_paged_decode_append(const void* q, const void* k_new, const void* v_new,
   return decode(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                 num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, false, 1.f,
                 1.f, out, out_dtype, workspace, workspace_bytes, stream, &nt);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Split-K scratch of pa_paged_decode_append_noalloc: one array per GPU the
+// library runs on (a device variable has one instance per device), held until
+// the process ends.  Host code never uses the name `scratch` as an address:
+// each device's address comes from hipGetSymbolAddress, taken once with that
+// device current.
+constexpr int kMaxScratchDevices = 64;
+__device__ __align__(256) char scratch[PA_DECODE_SCRATCH_BYTES];
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+std::mutex g_scratch_mutex;
+
+// The current device's scratch address, or NULL if it cannot be found.
+void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_paged_decode_append_noalloc(const void* q, const void* k_new, const void* v_new,
+                                   const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                                   const int32_t* block_tables, int max_blocks_per_seq,
+                                   const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                   int num_kv_heads, int head_dim, int block_size,
+                                   int num_blocks, float scale, void* out, int out_dtype,
+                                   void* stream) {
+  const NewTokens nt{k_new, v_new, slot_mapping};
+  if (num_seqs > 0) {
+    const size_t need = pa_paged_decode_workspace_bytes(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq);
+    if (need > PA_DECODE_SCRATCH_BYTES) return PA_ERR_SCRATCH;
+  }
+  // Argument errors first, with no device call: without a workspace the
+  // checks report PA_ERR_WORKSPACE exactly when everything else is valid.
+  const int rc = decode(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                        scale, false, 1.f, 1.f, out, out_dtype, nullptr, 0, stream, &nt);
+  if (rc != PA_ERR_WORKSPACE) return rc;
+  void* ws = device_scratch();
+  if (!ws) return PA_ERR_HIP;
+  return decode(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, false, 1.f,
+                1.f, out, out_dtype, ws, PA_DECODE_SCRATCH_BYTES, stream, &nt);
 }
 
 int pa_paged_decode_append_fp8(const void* q, const void* k_new, const void* v_new,

@@ -241,6 +241,25 @@ def test_decode_append_argument_checks(lib):
     assert app(fp8=True) == PA_ERR_SHAPE  # v_scale 0
 
 
+def test_decode_append_noalloc_argument_checks(lib):
+    """Argument errors come back before any device call; a size whose workspace exceeds the
+    fixed scratch array is refused with PA_ERR_SCRATCH."""
+    def app(B=4, Hq=4, Hkv=2, D=128, BS=16, MBS=8, k_new=FAKE, q=FAKE):
+        return lib.pa_paged_decode_append_noalloc(q, k_new, FAKE, FAKE, FAKE, FAKE, FAKE, MBS,
+                                                  FAKE, B, Hq, Hkv, D, BS, 64, 0.0, FAKE, 0, None)
+    assert app(k_new=None) == PA_ERR_NULL
+    assert app(q=None) == PA_ERR_NULL
+    assert app(B=0, k_new=None) == PA_OK
+    assert app(D=80) == PA_ERR_UNSUPPORTED
+    assert app(Hq=6, Hkv=4) == PA_ERR_SHAPE
+    # 7B-shaped decode at 256 sequences needs ~120 MB of partials: above the 64 MiB scratch
+    assert pa.decode_workspace_bytes(256, 28, 4, 128, 16, 512) > pa.DECODE_SCRATCH_BYTES
+    assert app(B=256, Hq=28, Hkv=4, BS=16, MBS=512) == pa.PA_ERR_SCRATCH
+    assert pa.status_string(pa.PA_ERR_SCRATCH).startswith("PA_ERR_SCRATCH")
+    # the Qwen3-0.6B-shaped decode fits
+    assert pa.decode_workspace_bytes(64, 16, 8, 128, 256, 16) <= pa.DECODE_SCRATCH_BYTES
+
+
 def test_decode_graph_argument_checks(lib):
     h = ctypes.c_void_p()
 

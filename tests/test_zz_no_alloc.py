@@ -1,0 +1,72 @@
+"""The allocation-free fused store + decode (library-held scratch instead of a workspace) equals
+the same call with a caller workspace, bit for bit, on two calls in a row (the second smaller),
+outputs and caches; and it matches the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_86_amd as pa
+from gpu_util import as_f64, bf16, bits, device, i32, say
+from workloads import config, decode_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _both(c, dev, out_dtype):
+    """(noalloc output, caches) and (workspace output, caches) from identical starting pools."""
+    res = []
+    for fn in ("noalloc", "workspace"):
+        kc, vc = bf16(c.k_cache, dev), bf16(c.v_cache, dev)
+        out = torch.full((c.batch, c.num_q_heads, c.head_dim), float("nan"), dtype=out_dtype,
+                         device=dev)
+        args = (bf16(c.q, dev), bf16(c.k_new, dev), bf16(c.v_new, dev), i32(c.slot_mapping, dev),
+                kc, vc, i32(c.block_tables, dev), i32(c.context_lens, dev), c.scale, out)
+        if fn == "noalloc":
+            pa.paged_decode_append_noalloc(*args)
+        else:
+            ws = torch.full((pa.decode_workspace_bytes(c.batch, c.num_q_heads, c.num_kv_heads,
+                                                       c.head_dim, c.block_size,
+                                                       c.max_blocks_per_seq),),
+                            0x5A, dtype=torch.uint8, device=dev)
+            pa.paged_decode_append(*args, workspace=ws)
+        res.append((out, kc, vc))
+    torch.cuda.synchronize()
+    return res
+
+
+def test_noalloc_equals_workspace_call_twice():
+    dev = device()
+    big = config(2)  # Qwen3-0.6B-shaped decode: 64 sequences, 16 / 8 heads, block 256
+    rng = np.random.default_rng(4711)
+    small = decode_case(4711, rng.integers(1, 3000, size=5), 16, 8, 128, 256, nb_factor=1.3,
+                        max_blocks_per_seq=16)
+    for label, c, dt in (("64 sequences", big, torch.bfloat16), ("5 sequences", small,
+                                                                 torch.float32)):
+        say(f"[noalloc] {label}: B={c.batch}")
+        (o1, k1, v1), (o2, k2, v2) = _both(c, dev, dt)
+        assert torch.equal(o1, o2)
+        assert torch.equal(k1.view(torch.int16), k2.view(torch.int16))
+        assert torch.equal(v1.view(torch.int16), v2.view(torch.int16))
+        kc, vc = oracle.kvcache_store(c.k_new, c.v_new, c.slot_mapping, c.k_cache, c.v_cache)
+        assert np.array_equal(bits(k1), kc) and np.array_equal(bits(v1), vc)
+        ref = oracle.paged_decode(c.q, kc, vc, c.block_tables, c.context_lens,
+                                  np.float32(c.scale))
+        err = np.abs(as_f64(o1) - ref).max()
+        say(f"[noalloc] {label}: max|err| {err:.3e}")
+        assert err <= 1e-2
+
+
+def test_noalloc_refuses_sizes_beyond_the_scratch():
+    dev = device()
+    c = decode_case(4712, [10, 20], 28, 4, 128, 16, nb_factor=1.5, max_blocks_per_seq=512)
+    d = torch.empty((256, 28, 128), dtype=torch.float32, device=dev)
+    q = torch.zeros((256, 28, 128), dtype=torch.bfloat16, device=dev)
+    kn = torch.zeros((256, 4, 128), dtype=torch.bfloat16, device=dev)
+    slots = torch.full((256,), -1, dtype=torch.int32, device=dev)
+    tables = torch.full((256, 512), -1, dtype=torch.int32, device=dev)
+    lens = torch.zeros((256,), dtype=torch.int32, device=dev)
+    kc, vc = bf16(c.k_cache, dev), bf16(c.v_cache, dev)
+    with pytest.raises(pa.PagedAttnError) as e:
+        pa.paged_decode_append_noalloc(q, kn, kn, slots, kc, vc, tables, lens, None, d)
+    assert e.value.status == pa.PA_ERR_SCRATCH

@@ -279,9 +279,10 @@ int pa_paged_prefill_fp8(const void* q, const int32_t* cu_seqlens_q, int num_seq
  *   slot_mapping [batch], context_lens [batch] and block_tables
  *   [batch, tables_stride] (tables_stride <= max_blocks_per_seq) are HOST
  *   arrays: they are copied into pinned staging (rows batch..bucket-1 get
- *   slot -1, length 0 and table -1) and uploaded asynchronously; the host
- *   blocks only if the staging area it is about to refill (the one used four
- *   steps earlier) is still being uploaded.  out: device pointer that receives the
+ *   slot -1, length 0 and table -1) and uploaded asynchronously with one copy;
+ *   the host blocks only if the staging area it is about to refill (the one
+ *   used four steps earlier) is still being uploaded.  out: device pointer
+ *   that receives the
  *   batch's rows (NULL = leave them in the static output).  Must be called on
  *   the device the object was created on; consecutive runs of one object
  *   must use the same stream (or be ordered by the caller).
@@ -391,6 +392,17 @@ int pa_paged_gather(const void* cache, const int32_t* block_tables, int max_bloc
  * Asynchronous on `stream`; bytes == 0 is a no-op.
  */
 int pa_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
+/*
+ * Measurement aid: the next decode call made by the calling thread
+ * (pa_paged_decode*, including the fused and FP8 forms and the decode rows of
+ * pa_paged_attention_mixed) records start_event on its stream immediately
+ * before its main split kernel and end_event immediately after it (before the
+ * split merge), so the two events bracket that kernel alone.  Events are
+ * hipEvent_t handles the caller created (either may be NULL).  The request is
+ * consumed by that call.  Always returns PA_OK.
+ */
+int pa_decode_time_next_launch(void* start_event, void* end_event);
 
 /*
  * Host block manager with prefix caching (MinivLLM guide Step 3 §3.2 Block,

@@ -35,6 +35,7 @@ EXPORTED_SYMBOLS = (
     "pa_paged_prefill_fp8",
     "pa_paged_gather",
     "pa_stream_read",
+    "pa_decode_time_next_launch",
     "pa_kvcache_store_fp8",
     "pa_paged_decode_fp8_workspace_bytes",
     "pa_paged_decode_fp8",
@@ -100,6 +101,8 @@ def load_library() -> ctypes.CDLL:
     lib.pa_paged_gather.restype = I
     lib.pa_stream_read.argtypes = [P, Z, P, P]
     lib.pa_stream_read.restype = I
+    lib.pa_decode_time_next_launch.argtypes = [P, P]
+    lib.pa_decode_time_next_launch.restype = I
     lib.pa_kvcache_store_fp8.argtypes = [P, P, P, I, P, P, I, I, I, I, F, F, P]
     lib.pa_kvcache_store_fp8.restype = I
     lib.pa_paged_decode_fp8_workspace_bytes.argtypes = [I, I, I, I, I, I]
@@ -495,6 +498,14 @@ def stream_read(src, sink) -> None:
     rc = load_library().pa_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
                                        _stream(src.device))
     _raise_on("pa_stream_read", rc)
+
+
+def decode_time_next_launch(start_event, end_event) -> None:
+    """Measurement aid: the next decode call of this thread records the two torch.cuda.Event
+    objects (recorded once before, so that they exist) around its main split kernel."""
+    rc = load_library().pa_decode_time_next_launch(ctypes.c_void_p(start_event.cuda_event),
+                                                   ctypes.c_void_p(end_event.cuda_event))
+    _raise_on("pa_decode_time_next_launch", rc)
 
 
 def default_scale(head_dim: int) -> float:

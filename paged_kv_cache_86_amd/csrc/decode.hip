@@ -631,14 +631,18 @@ template <int D, int GT, bool KV8, bool APPEND>
 int launch_d(const DecodeArgs& a, int B, hipStream_t stream) {
   const unsigned nwg = (unsigned)((int64_t)B * a.hg * a.nsplit_max);
   const bool scalar_blk = (1 << a.bs_log2) >= split_tokens<D, KV8>();
-  if (a.long_splits) {  // planned only when a block holds a short split
-    if (!scalar_blk) return -2;
+  if (a.long_splits && !scalar_blk) return -2;  // planned only when a block holds a short split
+  hipEvent_t t_start = nullptr, t_end = nullptr;
+  take_decode_timing(&t_start, &t_end);
+  if (t_start && hipEventRecord(t_start, stream) != hipSuccess) return -1;
+  if (a.long_splits) {
     launch_main<D, GT, KV8, APPEND, true, true>(a, nwg, stream);
   } else {
     if (scalar_blk) launch_main<D, GT, KV8, APPEND, false, true>(a, nwg, stream);
     else launch_main<D, GT, KV8, APPEND, false, false>(a, nwg, stream);
   }
   if (hipGetLastError() != hipSuccess) return -1;
+  if (t_end && hipEventRecord(t_end, stream) != hipSuccess) return -1;
   return a.nsplit_max > 1 ? launch_decode_combine(a, B, D, GT, stream) : 0;
 }
 
@@ -700,6 +704,22 @@ int launch_head_dim(const DecodeArgs& a, int B, int head_dim, int gt, hipStream_
 }
 
 }  // namespace
+
+namespace {
+thread_local hipEvent_t t_pending_start = nullptr;
+thread_local hipEvent_t t_pending_end = nullptr;
+}  // namespace
+
+void set_decode_timing(hipEvent_t start, hipEvent_t end) {
+  t_pending_start = start;
+  t_pending_end = end;
+}
+
+void take_decode_timing(hipEvent_t* start, hipEvent_t* end) {
+  *start = t_pending_start;
+  *end = t_pending_end;
+  t_pending_start = t_pending_end = nullptr;
+}
 
 int launch_decode_combine(const DecodeArgs& a, int B, int head_dim, int gt, hipStream_t stream) {
   if (head_dim == 128) return launch_combine_d<128>(a, B, gt, stream);

@@ -475,6 +475,9 @@ int launch_mfma_d(const DecodeArgs& a, int B, hipStream_t stream) {
   const unsigned nwg = (unsigned)((int64_t)B * a.hg * a.nsplit_max);
   constexpr int S = kW * kNch * kCK;
   constexpr int DEPTH = KV8 ? kDepthFp8 : kDepth;
+  hipEvent_t t_start = nullptr, t_end = nullptr;
+  take_decode_timing(&t_start, &t_end);
+  if (t_start && hipEventRecord(t_start, stream) != hipSuccess) return -1;
   if ((1 << a.bs_log2) >= S)
     hipLaunchKernelGGL((paged_decode_mfma_kernel<D, kNch, DEPTH, KV8, APPEND, true>), dim3(nwg),
                        dim3(256), 0, stream, a);
@@ -482,6 +485,7 @@ int launch_mfma_d(const DecodeArgs& a, int B, hipStream_t stream) {
     hipLaunchKernelGGL((paged_decode_mfma_kernel<D, kNch, DEPTH, KV8, APPEND, false>), dim3(nwg),
                        dim3(256), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return -1;
+  if (t_end && hipEventRecord(t_end, stream) != hipSuccess) return -1;
   const int gt = (a.group + a.nsub - 1) / a.nsub;
   return a.nsplit_max > 1 ? launch_decode_combine(a, B, D, gt, stream) : 0;
 }

@@ -91,6 +91,12 @@ struct DecodeArgs {
 
 int launch_paged_decode(const DecodeArgs& args, int B, int head_dim, int gt, bool kv8,
                         bool append, bool mfma, hipStream_t stream);
+
+// Measurement aid: events the next decode launch of the calling thread records
+// on its stream right before and right after its main (split) kernel.
+void set_decode_timing(hipEvent_t start, hipEvent_t end);
+// The calling thread's pending events (cleared by the call); null when none.
+void take_decode_timing(hipEvent_t* start, hipEvent_t* end);
 int launch_paged_decode_mfma(const DecodeArgs& args, int B, int head_dim, bool kv8, bool append,
                              hipStream_t stream);
 // Merge kernel of both decode kernels: split partials -> outputs.

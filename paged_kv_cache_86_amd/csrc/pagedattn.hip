@@ -541,6 +541,11 @@ int pa_paged_gather(const void* cache, const int32_t* block_tables, int max_bloc
              : PA_ERR_HIP;
 }
 
+int pa_decode_time_next_launch(void* start_event, void* end_event) {
+  pa::set_decode_timing((hipEvent_t)start_event, (hipEvent_t)end_event);
+  return PA_OK;
+}
+
 int pa_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
   if (bytes == 0) return PA_OK;
   if (!src || !sink) return PA_ERR_NULL;

@@ -42,6 +42,12 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kMaxSplitBlocks = 512;  // short-split tokens / block size (block size >= 1)
 
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+
+// {lo, hi} -> a bf16 pair, each rounded to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16_pair(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{lo, hi}, bf16x2_v));
+}
 
 // One workgroup = one (sequence, head group, split).
 //
@@ -58,8 +64,18 @@ constexpr int kMaxSplitBlocks = 512;  // short-split tokens / block size (block 
 //
 // KV8 selects an FP8 (OCP E4M3) cache: a 16-byte load then carries 16 codes
 // instead of 8 bf16 values.  K codes are widened to bf16 pairs and take the
-// same v_dot2 path as bf16 keys; V codes are widened to fp32.  The per-tensor
-// K scale is folded into the score scale and the V scale into the outputs.
+// same v_dot2 path as bf16 keys.  V: a lane holds U = 2 rows of each chunk;
+// for each element its codes in the two rows are interleaved (v_perm) and
+// widened to one bf16 pair, so a single v_dot2 per element and query head adds
+// both rows' weighted values.  The weights p enter that product rounded to
+// bf16 and the softmax denominator sums the same rounded weights (relative
+// error of each weight at most 2^-9).  The per-tensor K scale is folded into
+// the score scale and the V scale into the outputs.
+//
+// With KV8 the running output of a query head is rescaled by alpha =
+// 2^(m_old - m_new) only when some lane's running max grew in the chunk:
+// otherwise alpha is exactly 1 and the multiply is skipped (same result, bit
+// for bit).  (For bf16 the branch costs more registers than it saves.)
 //
 // APPEND fuses the store of each sequence's new token: position ctx-1 is not
 // read from the cache but from k_new / v_new (quantized first for KV8, exactly
@@ -85,6 +101,7 @@ __device__ __forceinline__ void paged_decode_body(const DecodeArgs& a) {
   constexpr int CH = U * RPW;       // tokens per wave chunk
   constexpr int S = kWaves * NIT * CH;  // tokens per short split
   constexpr int SL = LONG ? 2 * S : S;  // tokens per long split
+  constexpr bool PAIR_V = KV8 && U == 2;  // V rows of a lane as bf16 pairs (see above)
   static_assert(!LONG || SCALAR_BLK, "long splits read scalar block ids");
 
   __shared__ int s_blk[SCALAR_BLK ? 1 : kMaxSplitBlocks];
@@ -332,41 +349,75 @@ __device__ __forceinline__ void paged_decode_body(const DecodeArgs& a) {
           s[u][h] = ok[u] ? mul_rn(d, a.scale_log2e) : -INFINITY;
         }
       }
+      float alpha[GT];
+      uint32_t pp[GT];  // PAIR_V: the weights of rows u = 0, 1 as a bf16 pair
+      bool grew = false;
 #pragma unroll
       for (int h = 0; h < GT; ++h) {
         float mx = s[0][h];
 #pragma unroll
         for (int u = 1; u < U; ++u) mx = fmaxf(mx, s[u][h]);
         const float mnew = fmaxf(m[h], mx);
-        const float alpha = __builtin_amdgcn_exp2f(m[h] - mnew);
+        grew |= mnew != m[h];
+        alpha[h] = __builtin_amdgcn_exp2f(m[h] - mnew);
         m[h] = mnew;
         float psum = 0.f;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          s[u][h] = __builtin_amdgcn_exp2f(s[u][h] - mnew);
-          psum += s[u][h];
+        for (int u = 0; u < U; ++u) s[u][h] = __builtin_amdgcn_exp2f(s[u][h] - mnew);
+        if constexpr (PAIR_V) {
+          pp[h] = pack_bf16_pair(s[0][h], s[1][h]);
+          psum = bf16lo(pp[h]) + bf16hi(pp[h]);
+        } else {
+#pragma unroll
+          for (int u = 0; u < U; ++u) psum += s[u][h];
         }
-        l[h] = l[h] * alpha + psum;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+        l[h] = l[h] * alpha[h] + psum;
       }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        // Masked rows contribute p = 0; zeroing V as well keeps a NaN in an
-        // unused slot from turning 0 * NaN into NaN.
-        // (Selected per component: a select of the whole vector makes the
-        // compiler keep extra copies of the preloaded rows live.)
-        u32x4 vm;
-        vm.x = ok[u] ? vc[u].x : 0u;
-        vm.y = ok[u] ? vc[u].y : 0u;
-        vm.z = ok[u] ? vc[u].z : 0u;
-        vm.w = ok[u] ? vc[u].w : 0u;
-        float vf[EPL];
-        vconv(vm, vf);
+      if (!PAIR_V || __any(grew)) {
 #pragma unroll
         for (int h = 0; h < GT; ++h) {
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(s[u][h], vf[e], acc[h][e]);
+          for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha[h];
+        }
+      }
+      // Masked rows contribute p = 0; zeroing V as well keeps a NaN in an
+      // unused slot from turning 0 * NaN into NaN.
+      // (Selected per component: a select of the whole vector makes the
+      // compiler keep extra copies of the preloaded rows live.)
+      u32x4 vm[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        vm[u].x = ok[u] ? vc[u].x : 0u;
+        vm[u].y = ok[u] ? vc[u].y : 0u;
+        vm[u].z = ok[u] ? vc[u].z : 0u;
+        vm[u].w = ok[u] ? vc[u].w : 0u;
+      }
+      if constexpr (PAIR_V) {
+        const uint32_t w0[4] = {vm[0].x, vm[0].y, vm[0].z, vm[0].w};
+        const uint32_t w1[4] = {vm[1].x, vm[1].y, vm[1].z, vm[1].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // codes of elements 4e, 4e+1 (lo) and 4e+2, 4e+3 (hi) as {row 0, row 1} byte pairs
+          const uint32_t lo = __builtin_amdgcn_perm(w1[e], w0[e], 0x05010400u);
+          const uint32_t hi = __builtin_amdgcn_perm(w1[e], w0[e], 0x07030602u);
+          const uint32_t vb[4] = {fp8x2_to_bf16x2<false>(lo), fp8x2_to_bf16x2<true>(lo),
+                                  fp8x2_to_bf16x2<false>(hi), fp8x2_to_bf16x2<true>(hi)};
+#pragma unroll
+          for (int h = 0; h < GT; ++h) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) acc[h][4 * e + k] = dot2_bf16(pp[h], vb[k], acc[h][4 * e + k]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          float vf[EPL];
+          vconv(vm[u], vf);
+#pragma unroll
+          for (int h = 0; h < GT; ++h) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(s[u][h], vf[e], acc[h][e]);
+          }
         }
       }
     }

@@ -41,6 +41,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kMaxSplitBlocks = 512;  // short-split tokens / block size (block size >= 1)
+constexpr float kStaleLog2 = 8.f;     // KV8: growth of a running max (exp2 units) that forces a rescale
 
 typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
 
@@ -72,10 +73,13 @@ __device__ __forceinline__ uint32_t pack_bf16_pair(float lo, float hi) {
 // error of each weight at most 2^-9).  The per-tensor K scale is folded into
 // the score scale and the V scale into the outputs.
 //
-// With KV8 the running output of a query head is rescaled by alpha =
-// 2^(m_old - m_new) only when some lane's running max grew in the chunk:
-// otherwise alpha is exactly 1 and the multiply is skipped (same result, bit
-// for bit).  (For bf16 the branch costs more registers than it saves.)
+// With KV8 a row slot's running max m may also go stale: scores are weighted
+// by p = 2^(s - m) with m kept until some score of the wave exceeds its slot's
+// m by more than 2^8 (exp2 units), and only then do the slots move to their
+// true maxima and rescale l and the outputs.  The state (m, l, o) is valid for
+// any m, p stays <= 256, and the merges below take each slot's own m.  (The
+// bf16 kernel keeps the exact update: the branch costs it more registers than
+// it saves.)
 //
 // APPEND fuses the store of each sequence's new token: position ctx-1 is not
 // read from the cache but from k_new / v_new (quantized first for KV8, exactly
@@ -349,35 +353,53 @@ __device__ __forceinline__ void paged_decode_body(const DecodeArgs& a) {
           s[u][h] = ok[u] ? mul_rn(d, a.scale_log2e) : -INFINITY;
         }
       }
-      float alpha[GT];
       uint32_t pp[GT];  // PAIR_V: the weights of rows u = 0, 1 as a bf16 pair
-      bool grew = false;
-#pragma unroll
-      for (int h = 0; h < GT; ++h) {
-        float mx = s[0][h];
-#pragma unroll
-        for (int u = 1; u < U; ++u) mx = fmaxf(mx, s[u][h]);
-        const float mnew = fmaxf(m[h], mx);
-        grew |= mnew != m[h];
-        alpha[h] = __builtin_amdgcn_exp2f(m[h] - mnew);
-        m[h] = mnew;
-        float psum = 0.f;
-#pragma unroll
-        for (int u = 0; u < U; ++u) s[u][h] = __builtin_amdgcn_exp2f(s[u][h] - mnew);
-        if constexpr (PAIR_V) {
-          pp[h] = pack_bf16_pair(s[0][h], s[1][h]);
-          psum = bf16lo(pp[h]) + bf16hi(pp[h]);
-        } else {
-#pragma unroll
-          for (int u = 0; u < U; ++u) psum += s[u][h];
-        }
-        l[h] = l[h] * alpha[h] + psum;
-      }
-      if (!PAIR_V || __any(grew)) {
+      if constexpr (PAIR_V) {
+        // Stale max: a row slot keeps its running max until a score exceeds
+        // it by more than kStaleLog2 (so p <= 2^8); then every lane of the
+        // wave moves to its true max and rescales.
+        float mx[GT];
+        bool need = false;
 #pragma unroll
         for (int h = 0; h < GT; ++h) {
+          mx[h] = fmaxf(s[0][h], s[1][h]);
+          need |= mx[h] > m[h] + kStaleLog2;
+        }
+        if (__any(need)) {
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha[h];
+          for (int h = 0; h < GT; ++h) {
+            const float mnew = fmaxf(m[h], mx[h]);
+            const float alpha = __builtin_amdgcn_exp2f(m[h] - mnew);
+            m[h] = mnew;
+            l[h] *= alpha;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < GT; ++h) {
+          pp[h] = pack_bf16_pair(__builtin_amdgcn_exp2f(s[0][h] - m[h]),
+                                 __builtin_amdgcn_exp2f(s[1][h] - m[h]));
+          l[h] += bf16lo(pp[h]) + bf16hi(pp[h]);
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < GT; ++h) {
+          float mx = s[0][h];
+#pragma unroll
+          for (int u = 1; u < U; ++u) mx = fmaxf(mx, s[u][h]);
+          const float mnew = fmaxf(m[h], mx);
+          const float alpha = __builtin_amdgcn_exp2f(m[h] - mnew);
+          m[h] = mnew;
+          float psum = 0.f;
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            s[u][h] = __builtin_amdgcn_exp2f(s[u][h] - mnew);
+            psum += s[u][h];
+          }
+          l[h] = l[h] * alpha + psum;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
         }
       }
       // Masked rows contribute p = 0; zeroing V as well keeps a NaN in an

@@ -812,9 +812,12 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int head_dim, int block_size, int
   p.gt = (p.group + p.nsub - 1) / p.nsub;
   const int64_t max_ctx = (int64_t)mbs * block_size;
   const int64_t units = (int64_t)B * Hkv * p.nsub;
-  const int S = p.mfma ? kMfmaSplitTokens
-                : head_dim == 64 ? (kv8 ? split_tokens<64, true>() : split_tokens<64, false>())
-                                 : (kv8 ? split_tokens<128, true>() : split_tokens<128, false>());
+  int S = p.mfma ? kMfmaSplitTokens
+          : head_dim == 64 ? (kv8 ? split_tokens<64, true>() : split_tokens<64, false>())
+                           : (kv8 ? split_tokens<128, true>() : split_tokens<128, false>());
+  if (p.mfma && max_ctx > kMfmaSplitTokens &&
+      units * ((max_ctx + kMfmaLongSplitTokens - 1) / kMfmaLongSplitTokens) >= kMfmaLongMinGrid)
+    S = kMfmaLongSplitTokens;
   int sl = 0;
   while ((1 << sl) < S) ++sl;
   p.split_log2 = sl;

@@ -48,7 +48,6 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kW = 4;             // waves per workgroup
 constexpr int kCK = 32;           // keys per wave chunk: two 16-key MFMA tiles
-constexpr int kMaxSplitIds = 512; // staged block ids of one split
 constexpr int kQR = 16;           // query heads per workgroup (one MFMA side)
 
 __device__ __forceinline__ f32x4_t mfma16(const u32x4& a, const u32x4& b, const f32x4_t& c) {
@@ -94,7 +93,7 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
 
   // V staging during the loop; the per-wave unnormalised O for the merge afterwards.
   __shared__ __align__(16) char s_v[LDS_V > LDS_O ? LDS_V : LDS_O];
-  __shared__ int s_blk[SCALAR_BLK ? 1 : kMaxSplitIds];
+  __shared__ int s_blk[SCALAR_BLK ? 1 : S];  // staged block ids of the split (block size >= 1)
   __shared__ float s_m[kW][kQR];
   __shared__ float s_l[kW][kQR];
 
@@ -137,7 +136,7 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
   } else {
     const int nb = S >> a.bs_log2;
 #pragma unroll
-    for (int k = 0; k < kMaxSplitIds / 256; ++k) {
+    for (int k = 0; k < (S + 255) / 256; ++k) {
       const int i = tid + 256 * k;
       if (i < nb) {
         const int b = b0 + i < a.mbs ? trow[b0 + i] : -1;
@@ -292,7 +291,8 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
   float m = kNegBig;  // running max (log2 units) of this lane's query head
   const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0
 
-  auto compute_chunk = [&](int it, const Chunk& ch) {
+  // `refill` runs once the chunk's rows are in LDS (its registers are free).
+  auto compute_chunk = [&](int it, const Chunk& ch, auto&& refill) {
     const int k0 = t0 + (it * kW + w) * kCK;
     // K rows through this wave's LDS area into the operand layout, then V rows
     // (read back transposed below; the wave's LDS accesses stay in order).
@@ -308,6 +308,7 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
       }
     }
     put_rows(ch.v, ch.ok);
+    refill();
     // Scores of keys k0 + 16 kt + 4 g + e (log2 units), masked to -inf.
     float s[2][4];
     float mx = -INFINITY;
@@ -356,14 +357,23 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
     lacc = mfma16(ones, pb, lacc);
   };
 
+  // Chunks in groups of DEPTH (a loop: unrolled over all NCH chunks, the
+  // compiler keeps more chunks' rows live than the registers of three waves
+  // per SIMD hold); buffer d serves chunks it0 + d and is refilled with chunk
+  // it0 + d + DEPTH as soon as its rows are staged in LDS, so at most DEPTH
+  // chunks are held in registers.
+  static_assert(NCH % DEPTH == 0, "whole groups of DEPTH chunks");
   Chunk buf[DEPTH];
 #pragma unroll
-  for (int it = 0; it < DEPTH; ++it) load_chunk(it, buf[it]);
+  for (int d = 0; d < DEPTH; ++d) load_chunk(d, buf[d]);
+#pragma unroll 1
+  for (int it0 = 0; it0 < NCH; it0 += DEPTH) {
 #pragma unroll
-  for (int it = 0; it < NCH; ++it) {
-    Chunk cur = buf[it % DEPTH];
-    if (it + DEPTH < NCH) load_chunk(it + DEPTH, buf[it % DEPTH]);
-    compute_chunk(it, cur);
+    for (int d = 0; d < DEPTH; ++d) {
+      compute_chunk(it0 + d, buf[d], [&]() {
+        if (it0 + d + DEPTH < NCH) load_chunk(it0 + d + DEPTH, buf[d]);
+      });
+    }
   }
 
   // APPEND: wave 0 of the sequence's last split folds in the new token
@@ -461,29 +471,45 @@ void paged_decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
-// Production tiling: 2 chunks of 32 keys per wave (a split is 256 tokens),
-// both in flight.
+// Production tilings.  Short splits: 2 chunks of 32 keys per wave (a split
+// is 256 tokens), both in flight.  Long splits: 16 chunks per wave (2048
+// tokens), one in flight (refilled as soon as the current chunk is staged
+// in LDS; two held in registers would spill at three waves per SIMD).  The
+// long split pays the workgroup's set-up, merge and partial write over 8x
+// the tokens: 7B-shaped decode (256 sequences, 28/4 heads, block 16)
+// 460 -> 386-389 us per step.
 constexpr int kNch = 2;
-// Chunks in flight per wave: both for bf16 pools; one for FP8 pools, whose
-// widening work per chunk already hides the load latency (7B-shaped FP8
-// decode: 292-298 -> 279-281 us; bf16 is level or slower with one).
+constexpr int kNchLong = 16;
+static_assert(kW * kNch * kCK == kMfmaSplitTokens, "short split length");
+static_assert(kW * kNchLong * kCK == kMfmaLongSplitTokens, "long split length");
+// Chunks in flight per wave in a short split: both for bf16 pools; one for
+// FP8 pools, whose widening work per chunk already hides the load latency
+// (7B-shaped FP8 decode: 292-298 -> 279-281 us; bf16 is level or slower with
+// one).
 constexpr int kDepth = 2;
 constexpr int kDepthFp8 = 1;
+
+template <int D, int NCH, int DEPTH, bool KV8, bool APPEND>
+void launch_mfma_kernel(const DecodeArgs& a, unsigned nwg, hipStream_t stream) {
+  constexpr int S = kW * NCH * kCK;
+  if ((1 << a.bs_log2) >= S)
+    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, NCH, DEPTH, KV8, APPEND, true>), dim3(nwg),
+                       dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, NCH, DEPTH, KV8, APPEND, false>), dim3(nwg),
+                       dim3(256), 0, stream, a);
+}
 
 template <int D, bool KV8, bool APPEND>
 int launch_mfma_d(const DecodeArgs& a, int B, hipStream_t stream) {
   const unsigned nwg = (unsigned)((int64_t)B * a.hg * a.nsplit_max);
-  constexpr int S = kW * kNch * kCK;
-  constexpr int DEPTH = KV8 ? kDepthFp8 : kDepth;
+  const bool long_split = (1 << a.split_log2) == kMfmaLongSplitTokens;
+  if (!long_split && (1 << a.split_log2) != kMfmaSplitTokens) return -2;
   hipEvent_t t_start = nullptr, t_end = nullptr;
   take_decode_timing(&t_start, &t_end);
   if (t_start && hipEventRecord(t_start, stream) != hipSuccess) return -1;
-  if ((1 << a.bs_log2) >= S)
-    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, kNch, DEPTH, KV8, APPEND, true>), dim3(nwg),
-                       dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, kNch, DEPTH, KV8, APPEND, false>), dim3(nwg),
-                       dim3(256), 0, stream, a);
+  if (long_split) launch_mfma_kernel<D, kNchLong, 1, KV8, APPEND>(a, nwg, stream);
+  else launch_mfma_kernel<D, kNch, KV8 ? kDepthFp8 : kDepth, KV8, APPEND>(a, nwg, stream);
   if (hipGetLastError() != hipSuccess) return -1;
   if (t_end && hipEventRecord(t_end, stream) != hipSuccess) return -1;
   const int gt = (a.group + a.nsub - 1) / a.nsub;

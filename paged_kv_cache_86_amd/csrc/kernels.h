@@ -30,11 +30,16 @@ constexpr int64_t kLongSplitMinGridFp8 = 1024;
 constexpr int kCompactPerLane = 4;
 constexpr int kCompactMaxSeqs = 64 * kCompactPerLane;
 // Query heads per KV head from which decode runs on MFMA (bf16 and FP8
-// pools), the most heads one MFMA workgroup serves, and its split length.
+// pools), the most heads one MFMA workgroup serves, and its split lengths:
+// long splits when the grid with them still has kMfmaLongMinGrid workgroups
+// (8 per compute unit), short ones otherwise (small batches keep enough
+// workgroups to fill the device).
 constexpr int kMfmaMinGroup = 3;
 constexpr int kMfmaMinGroupFp8 = 3;
 constexpr int kMfmaMaxGt = 16;
 constexpr int kMfmaSplitTokens = 256;
+constexpr int kMfmaLongSplitTokens = 2048;
+constexpr int64_t kMfmaLongMinGrid = 2048;
 
 int launch_kvcache_store(const void* k, const void* v, const int32_t* slot_mapping, int T,
                          void* k_cache, void* v_cache, int num_blocks, int block_size,
@@ -58,6 +63,11 @@ struct DecodePlan {
   bool compact;      // workgroups take compacted (sequence, split) items
   int64_t units;   // (sequence, head group) pairs
   size_t ml_bytes, o_bytes;  // workspace regions: (max, sum) pairs, then unnormalised outputs
+  // Splits longer than the kernel's short split (VALU long splits, or the
+  // MFMA kernel's long split length): chosen from some batch size up.
+  bool coarse() const {
+    return long_splits || (mfma && (1 << split_log2) == kMfmaLongSplitTokens);
+  }
   size_t workspace_bytes() const { return ml_bytes + o_bytes; }
 };
 

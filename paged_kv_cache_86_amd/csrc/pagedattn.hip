@@ -76,10 +76,11 @@ namespace {
 
 // Workspace of a decode call with num_seqs sequences: the most any batch of
 // 1 .. num_seqs sequences needs, so one workspace serves every smaller batch.
-// A plan's own size grows with the batch except where long splits switch on
-// (half the partial slots per sequence); that happens once, at a threshold
-// batch, so the maximum is the larger of the plan at num_seqs and the plan
-// just below the threshold.
+// A plan's own size grows with the batch except where longer splits switch
+// on (VALU long splits: half the partial slots per sequence; MFMA long
+// splits: an eighth); that happens once, at a threshold batch, so the maximum
+// is the larger of the plan at num_seqs and the plan just below the
+// threshold.
 size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                               int block_size, int max_blocks_per_seq, bool kv8) {
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
@@ -89,13 +90,13 @@ size_t decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads, i
                                            block_size, max_blocks_per_seq, kv8);
   if (p.units > pa::kDecodeMaxUnits || p.nsplit_short > pa::kDecodeMaxSplits) return 0;
   size_t bytes = p.workspace_bytes();
-  if (p.long_splits) {
+  if (p.coarse()) {
     // largest batch below num_seqs whose plan keeps short splits
     int lo = 1, hi = num_seqs - 1, below = 0;
     while (lo <= hi) {
       const int mid = lo + (hi - lo) / 2;
       if (pa::plan_decode(mid, num_q_heads, num_kv_heads, head_dim, block_size,
-                          max_blocks_per_seq, kv8).long_splits) {
+                          max_blocks_per_seq, kv8).coarse()) {
         hi = mid - 1;
       } else {
         below = mid;

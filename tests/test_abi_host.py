@@ -252,12 +252,14 @@ def test_decode_append_noalloc_argument_checks(lib):
     assert app(B=0, k_new=None) == PA_OK
     assert app(D=80) == PA_ERR_UNSUPPORTED
     assert app(Hq=6, Hkv=4) == PA_ERR_SHAPE
-    # 7B-shaped decode at 256 sequences needs ~120 MB of partials: above the 64 MiB scratch
-    assert pa.decode_workspace_bytes(256, 28, 4, 128, 16, 512) > pa.DECODE_SCRATCH_BYTES
-    assert app(B=256, Hq=28, Hkv=4, BS=16, MBS=512) == pa.PA_ERR_SCRATCH
+    # 7B-shaped decode at 256 sequences with 65,536-token tables needs ~119 MB of partials
+    # (the most any batch up to 256 needs): above the 64 MiB scratch
+    assert pa.decode_workspace_bytes(256, 28, 4, 128, 16, 4096) > pa.DECODE_SCRATCH_BYTES
+    assert app(B=256, Hq=28, Hkv=4, BS=16, MBS=4096) == pa.PA_ERR_SCRATCH
     assert pa.status_string(pa.PA_ERR_SCRATCH).startswith("PA_ERR_SCRATCH")
-    # the Qwen3-0.6B-shaped decode fits
-    assert pa.decode_workspace_bytes(64, 16, 8, 128, 256, 16) <= pa.DECODE_SCRATCH_BYTES
+    # the Qwen3-0.6B-shaped, 7B-shaped (8,192-token tables) and 512-sequence decodes fit
+    for args in ((64, 16, 8, 128, 256, 16), (256, 28, 4, 128, 16, 512), (512, 16, 8, 128, 256, 16)):
+        assert 0 < pa.decode_workspace_bytes(*args) <= pa.DECODE_SCRATCH_BYTES
 
 
 def test_decode_graph_argument_checks(lib):

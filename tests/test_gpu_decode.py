@@ -279,6 +279,43 @@ def test_decode_long_splits(D, BS):
     check_append(c, dev, f"long splits D{D} BS{BS}")
 
 
+def _mfma_long_case(seed, D, BS, B=128):
+    """B x 28/4 heads (7 query heads per KV head: the MFMA kernel) with 8,192-token tables: at
+    128 sequences the grid with 2,048-token splits still has 2,048 workgroups, so the long
+    split length is taken; contexts at both split lengths' boundaries, the rest uniform."""
+    S, L = 256, 2048
+    edges = [1, 2, S - 1, S, S + 1, L - 1, L, L + 1, 2 * L - 1, 2 * L, 2 * L + 1, 3 * L + S,
+             4 * L - 1, 4 * L, 0, 17]
+    rng = np.random.default_rng(seed)
+    ctx = edges + [int(x) for x in rng.integers(1, 4 * L, B - len(edges), endpoint=True)]
+    return decode_case(seed, ctx, 28, 4, D, BS, nb_factor=1.1, max_blocks_per_seq=4 * L // BS)
+
+
+@pytest.mark.parametrize("D,BS", [(128, 16), (64, 1), (128, 1024)])
+def test_decode_mfma_long_splits(D, BS):
+    """The MFMA kernel's 2,048-token splits (one chunk of loads in flight per wave, the block
+    ids of a split staged in LDS — 2,048 of them at block size 1 — or a split over two blocks):
+    every sequence against the oracle, plain and fused store."""
+    dev = device()
+    c = _mfma_long_case(5151 + D + BS, D, BS)
+    B = c.batch
+    # the switch to long splits happens at 128 sequences: the size is the most a smaller
+    # batch with short splits needs
+    ws = [pa.decode_workspace_bytes(b, 28, 4, D, BS, c.max_blocks_per_seq) for b in (126, 127, B)]
+    assert ws[0] < ws[1] == ws[2]
+    say(f"[decode-mfma-long] D={D} BS={BS} B={B} ctx max {int(c.context_lens.max())}")
+    d = DecodeOnDevice(c, dev)
+    d.store()
+    out32 = as_f64(d.decode(torch.float32))
+    kc, vc = oracle.kvcache_store(c.k_new, c.v_new, c.slot_mapping, c.k_cache, c.v_cache)
+    ref = oracle.paged_decode(c.q, kc, vc, c.block_tables, c.context_lens, np.float32(c.scale))
+    err = np.abs(out32 - ref).max()
+    say(f"[decode-mfma-long] D={D} BS={BS}: max|err| {err:.3e}")
+    assert err <= ATOL
+    assert np.all(out32[list(c.context_lens).index(0)] == 0)
+    check_append(c, dev, f"mfma long splits D{D} BS{BS}", ref=ref)
+
+
 MAX_CASES = [(128, 2), (128, 7), (64, 2), (64, 7)]  # VALU (2 heads per KV head) and MFMA (7)
 
 

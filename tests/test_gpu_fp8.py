@@ -306,6 +306,41 @@ def test_decode_fp8_long_splits():
     assert err <= ATOL
 
 
+def test_decode_fp8_mfma_long_splits():
+    """7 query heads per KV head on an FP8 pool, 128 sequences with 8,192-token tables at block
+    16: the MFMA kernel's 2,048-token splits, every boundary of both split lengths, plain and
+    fused store, every sequence against the oracle."""
+    dev = device()
+    S, L = 256, 2048
+    edges = [1, 2, S - 1, S, S + 1, L - 1, L, L + 1, 2 * L, 2 * L + 1, 4 * L - 1, 4 * L, 0, 33]
+    rng = np.random.default_rng(5252)
+    ctx = edges + [int(x) for x in rng.integers(1, 4 * L, 128 - len(edges), endpoint=True)]
+    c = decode_case(5252, ctx, 28, 4, 128, 16, nb_factor=1.1, max_blocks_per_seq=4 * L // 16)
+    say(f"[fp8-mfma-long] B=128 ctx max {int(c.context_lens.max())}")
+    check_decode(Fp8Pool(c, dev, 0.0125, 0.02), label="mfma long splits")
+    ks, vs = 0.0125, 0.02
+    NB = c.k_cache.shape[0]
+    kc = torch.empty((NB, 16, 4, 128), dtype=torch.uint8, device=dev)
+    vc = torch.empty_like(kc)
+    every = np.arange(NB * 16, dtype=np.int32)
+    pa.kvcache_store_fp8(bf16(c.k_cache.reshape(NB * 16, 4, 128), dev),
+                         bf16(c.v_cache.reshape(NB * 16, 4, 128), dev), i32(every, dev), kc, vc,
+                         ks, vs)
+    out = torch.empty((128, 28, 128), dtype=torch.float32, device=dev)
+    pa.paged_decode_append_fp8(bf16(c.q, dev), bf16(c.k_new, dev), bf16(c.v_new, dev),
+                               i32(c.slot_mapping, dev), kc, vc, i32(c.block_tables, dev),
+                               i32(c.context_lens, dev), c.scale, ks, vs, out)
+    kc8, vc8 = oracle.kvcache_store_fp8(c.k_new, c.v_new, c.slot_mapping,
+                                        oracle.quantize(c.k_cache, ks),
+                                        oracle.quantize(c.v_cache, vs), ks, vs)
+    assert np.array_equal(codes(kc), kc8) and np.array_equal(codes(vc), vc8)
+    ref = oracle.paged_decode_fp8(c.q, kc8, vc8, c.block_tables, c.context_lens,
+                                  np.float32(c.scale), ks, vs)
+    err = np.abs(as_f64(out) - ref).max()
+    say(f"[fp8-mfma-long] fused store: max|err| {err:.3e}")
+    assert err <= ATOL
+
+
 FP8_MAX_CASES = [(2, 1), (7, 1)]  # VALU (long splits: 8 sequences x 128 slots), MFMA
 
 

@@ -64,7 +64,7 @@ def test_noalloc_refuses_sizes_beyond_the_scratch():
     q = torch.zeros((256, 28, 128), dtype=torch.bfloat16, device=dev)
     kn = torch.zeros((256, 4, 128), dtype=torch.bfloat16, device=dev)
     slots = torch.full((256,), -1, dtype=torch.int32, device=dev)
-    tables = torch.full((256, 512), -1, dtype=torch.int32, device=dev)
+    tables = torch.full((256, 4096), -1, dtype=torch.int32, device=dev)  # 65,536-token tables
     lens = torch.zeros((256,), dtype=torch.int32, device=dev)
     kc, vc = bf16(c.k_cache, dev), bf16(c.v_cache, dev)
     with pytest.raises(pa.PagedAttnError) as e:

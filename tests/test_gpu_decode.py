@@ -342,6 +342,30 @@ def test_decode_max_context(D, Hq):
     check_append(c, dev, f"max context D{D} h{Hq}/1")
 
 
+def test_decode_mfma_long_splits_max_context():
+    """The longest context on the MFMA kernel's 2,048-token splits: 8 sequences x 56/8 heads
+    (7 per KV head) with 65,536-token tables is the smallest batch whose grid takes them (32
+    splits per context, merged past the merge's first 16-split batch), next to one-token,
+    empty and boundary contexts; store then decode, and the fused call."""
+    dev = device()
+    maxc, BS = 65536, 256
+    ctx = [maxc, 1, maxc - 1, 300, 2048, 2049, 0, 4097]
+    c = decode_case(9177, ctx, 56, 8, 128, BS, nb_factor=1.05, max_blocks_per_seq=maxc // BS)
+    ws = [pa.decode_workspace_bytes(b, 56, 8, 128, BS, maxc // BS) for b in (6, 7, 8)]
+    assert ws[0] < ws[1] == ws[2]  # long splits from 8 sequences on
+    say(f"[decode-mfma-long-max] 56/8 heads ctx={ctx}")
+    d = DecodeOnDevice(c, dev)
+    d.store()
+    out32 = as_f64(d.decode(torch.float32))
+    kc, vc = oracle.kvcache_store(c.k_new, c.v_new, c.slot_mapping, c.k_cache, c.v_cache)
+    ref = oracle.paged_decode(c.q, kc, vc, c.block_tables, c.context_lens, np.float32(c.scale))
+    err = np.abs(out32 - ref).max()
+    say(f"[decode-mfma-long-max] max|err| {err:.3e}")
+    assert err <= ATOL
+    assert np.all(out32[6] == 0)
+    check_append(c, dev, "mfma long splits, max context", ref=ref)
+
+
 COMPACT_CASES = [(4, 2, 256), (14, 2, 16)]  # (Hq, Hkv, block size): VALU kernel, MFMA kernel
 
 

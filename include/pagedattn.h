@@ -116,7 +116,10 @@ size_t pa_paged_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv
  *   scale         multiplies q.k (fp32); scale <= 0 selects 1/sqrt(head_dim)
  *   out           [B, num_q_heads, head_dim], bf16 (round to nearest even) or fp32
  *   workspace     see pa_paged_decode_workspace_bytes
- * out[i,h] = softmax(scale * q[i,h] . K_i^T) V_i, fp32 accumulation.
+ * out[i,h] = softmax(scale * q[i,h] . K_i^T) V_i, fp32 accumulation.  With
+ * three or more query heads per KV head (the matrix-core path) the attention
+ * weights enter the V product rounded to bf16 (relative error at most 2^-9
+ * each, the softmax denominator summing the same rounded weights).
  * Deterministic: the same inputs give bit-identical outputs.  Runs as one or
  * two kernels on `stream` (partials, then a merge when a context spans
  * more than one split).
@@ -202,10 +205,12 @@ size_t pa_paged_decode_fp8_workspace_bytes(int num_seqs, int num_q_heads, int nu
 /*
  * pa_paged_decode on FP8 pools (layout above): attention over the
  * dequantized keys decode(code) * k_scale and values decode(code) * v_scale;
- * q and out as for pa_paged_decode.  The codes are widened exactly (K to
- * bf16, V to fp32); k_scale is folded into the score scale and v_scale
- * multiplies the merged outputs, so the only rounding beyond the bf16 path is
- * that of the products.  k_scale and v_scale must be finite and > 0.
+ * q and out as for pa_paged_decode.  The codes are widened exactly to bf16
+ * (every E4M3 value is a bf16 value); k_scale is folded into the score scale
+ * and v_scale multiplies the merged outputs.  The attention weights enter the
+ * V product rounded to bf16 (relative error at most 2^-9 each, the softmax
+ * denominator summing the same rounded weights), for every head-group size.
+ * k_scale and v_scale must be finite and > 0.
  * Limits, workspace rules and determinism as for pa_paged_decode.
  */
 int pa_paged_decode_fp8(const void* q, const void* k_cache, const void* v_cache,

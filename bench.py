@@ -152,8 +152,8 @@ def timed_loop(torch, fn_pre, fn_main, steps, warmup, flush):
 
 def kernel_times(torch, pa, fn, steps, flush):
     """Event-timed duration (ms) of the main decode kernel of `steps` calls of fn, each
-    preceded by a cache flush: the library records the two events on the call's stream
-    right before and right after that kernel (pa_decode_time_next_launch)."""
+    preceded by a cache flush: the library attaches the two events to that kernel's launch,
+    so they carry its own start and end times (pa_decode_time_next_launch)."""
     pairs = []
     for _ in range(steps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -401,11 +401,12 @@ int pa_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 /*
  * Measurement aid: the next decode call made by the calling thread
  * (pa_paged_decode*, including the fused and FP8 forms and the decode rows of
- * pa_paged_attention_mixed) records start_event on its stream immediately
- * before its main split kernel and end_event immediately after it (before the
- * split merge), so the two events bracket that kernel alone.  Events are
- * hipEvent_t handles the caller created (either may be NULL).  The request is
- * consumed by that call.  Always returns PA_OK.
+ * pa_paged_attention_mixed) attaches start_event and end_event to the launch
+ * of its main split kernel (hipExtLaunchKernel), so the two events carry that
+ * kernel's own start and end times: no separate event packets, and neither
+ * the store nor the split merge.  Events are hipEvent_t handles the caller
+ * created with timing enabled (either may be NULL).  The request is consumed
+ * by that call.  Always returns PA_OK.
  */
 int pa_decode_time_next_launch(void* start_event, void* end_event);
 

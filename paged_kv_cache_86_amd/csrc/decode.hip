@@ -30,6 +30,8 @@
 //     an in-kernel "last workgroup merges" scheme needs a device-scope
 //     release/acquire per workgroup, which on this chip writes back and
 //     invalidates the whole L2 of an XCD and costs far more than a launch.
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 #include "common.h"
@@ -692,12 +694,15 @@ constexpr int split_tokens() {
   return kWaves * tile_nit<KV8>() * tile_u<KV8>() * (64 / (D / (KV8 ? 16 : 8)));
 }
 
+// t_start / t_end (either may be null) are attached to the launch itself
+// (hipExtLaunchKernel), so they carry the kernel's own start and end times.
 template <int D, int GT, bool KV8, bool APPEND, bool LONG, bool SCALAR_BLK>
-void launch_main(const DecodeArgs& a, unsigned nwg, hipStream_t stream) {
-  hipLaunchKernelGGL((paged_decode_kernel<D, GT, tile_u<KV8>(), tile_nit<KV8>(), tile_depth<KV8>(),
-                                          tile_depth<KV8>() / 4, LONG, kNontemporal, KV8, APPEND,
-                                          SCALAR_BLK>),
-                     dim3(nwg), dim3(256), 0, stream, a);
+void launch_main(const DecodeArgs& a, unsigned nwg, hipStream_t stream, hipEvent_t t_start,
+                 hipEvent_t t_end) {
+  hipExtLaunchKernelGGL((paged_decode_kernel<D, GT, tile_u<KV8>(), tile_nit<KV8>(),
+                                             tile_depth<KV8>(), tile_depth<KV8>() / 4, LONG,
+                                             kNontemporal, KV8, APPEND, SCALAR_BLK>),
+                        dim3(nwg), dim3(256), 0, stream, t_start, t_end, 0u, a);
 }
 
 template <int D, int GT, bool KV8, bool APPEND>
@@ -707,15 +712,13 @@ int launch_d(const DecodeArgs& a, int B, hipStream_t stream) {
   if (a.long_splits && !scalar_blk) return -2;  // planned only when a block holds a short split
   hipEvent_t t_start = nullptr, t_end = nullptr;
   take_decode_timing(&t_start, &t_end);
-  if (t_start && hipEventRecord(t_start, stream) != hipSuccess) return -1;
   if (a.long_splits) {
-    launch_main<D, GT, KV8, APPEND, true, true>(a, nwg, stream);
+    launch_main<D, GT, KV8, APPEND, true, true>(a, nwg, stream, t_start, t_end);
   } else {
-    if (scalar_blk) launch_main<D, GT, KV8, APPEND, false, true>(a, nwg, stream);
-    else launch_main<D, GT, KV8, APPEND, false, false>(a, nwg, stream);
+    if (scalar_blk) launch_main<D, GT, KV8, APPEND, false, true>(a, nwg, stream, t_start, t_end);
+    else launch_main<D, GT, KV8, APPEND, false, false>(a, nwg, stream, t_start, t_end);
   }
   if (hipGetLastError() != hipSuccess) return -1;
-  if (t_end && hipEventRecord(t_end, stream) != hipSuccess) return -1;
   return a.nsplit_max > 1 ? launch_decode_combine(a, B, D, GT, stream) : 0;
 }
 

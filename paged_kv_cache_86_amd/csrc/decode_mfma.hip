@@ -33,6 +33,8 @@
 // K scale is folded into the score scale and the V scale multiplies the merged
 // outputs.  The fused store quantizes the new row exactly as the store kernel
 // does, and the new token is attended with the values its codes decode to.
+#include <hip/hip_ext.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -489,15 +491,18 @@ static_assert(kW * kNchLong * kCK == kMfmaLongSplitTokens, "long split length");
 constexpr int kDepth = 2;
 constexpr int kDepthFp8 = 1;
 
+// t_start / t_end (either may be null) are attached to the launch itself
+// (hipExtLaunchKernel), so they carry the kernel's own start and end times.
 template <int D, int NCH, int DEPTH, bool KV8, bool APPEND>
-void launch_mfma_kernel(const DecodeArgs& a, unsigned nwg, hipStream_t stream) {
+void launch_mfma_kernel(const DecodeArgs& a, unsigned nwg, hipStream_t stream, hipEvent_t t_start,
+                        hipEvent_t t_end) {
   constexpr int S = kW * NCH * kCK;
   if ((1 << a.bs_log2) >= S)
-    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, NCH, DEPTH, KV8, APPEND, true>), dim3(nwg),
-                       dim3(256), 0, stream, a);
+    hipExtLaunchKernelGGL((paged_decode_mfma_kernel<D, NCH, DEPTH, KV8, APPEND, true>), dim3(nwg),
+                          dim3(256), 0, stream, t_start, t_end, 0u, a);
   else
-    hipLaunchKernelGGL((paged_decode_mfma_kernel<D, NCH, DEPTH, KV8, APPEND, false>), dim3(nwg),
-                       dim3(256), 0, stream, a);
+    hipExtLaunchKernelGGL((paged_decode_mfma_kernel<D, NCH, DEPTH, KV8, APPEND, false>),
+                          dim3(nwg), dim3(256), 0, stream, t_start, t_end, 0u, a);
 }
 
 template <int D, bool KV8, bool APPEND>
@@ -507,11 +512,12 @@ int launch_mfma_d(const DecodeArgs& a, int B, hipStream_t stream) {
   if (!long_split && (1 << a.split_log2) != kMfmaSplitTokens) return -2;
   hipEvent_t t_start = nullptr, t_end = nullptr;
   take_decode_timing(&t_start, &t_end);
-  if (t_start && hipEventRecord(t_start, stream) != hipSuccess) return -1;
-  if (long_split) launch_mfma_kernel<D, kNchLong, 1, KV8, APPEND>(a, nwg, stream);
-  else launch_mfma_kernel<D, kNch, KV8 ? kDepthFp8 : kDepth, KV8, APPEND>(a, nwg, stream);
+  if (long_split)
+    launch_mfma_kernel<D, kNchLong, 1, KV8, APPEND>(a, nwg, stream, t_start, t_end);
+  else
+    launch_mfma_kernel<D, kNch, KV8 ? kDepthFp8 : kDepth, KV8, APPEND>(a, nwg, stream, t_start,
+                                                                        t_end);
   if (hipGetLastError() != hipSuccess) return -1;
-  if (t_end && hipEventRecord(t_end, stream) != hipSuccess) return -1;
   const int gt = (a.group + a.nsub - 1) / a.nsub;
   return a.nsplit_max > 1 ? launch_decode_combine(a, B, D, gt, stream) : 0;
 }

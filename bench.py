@@ -373,6 +373,8 @@ def main():
 
             ostep, _, oev, _ = timed_loop(torch, nothing, oappend, max(10, args.steps // 2),
                                           max(3, args.warmup // 2), flush)
+            o_kms = float(np.mean(kernel_times(torch, pa, oappend, max(10, args.steps // 2),
+                                               flush)))
             okv = o.kv_bytes()
             ukv = o.unique_kv_bytes()  # blocks shared by several sequences counted once
             oalg = decode_algorithmic_bytes(o) + store_bytes(o)
@@ -385,7 +387,9 @@ def main():
                 "achieved_gb_s": round(oalg / (ostep * 1e-3) / 1e9, 2),
                 "unique_kv_gb_s": round(ukv / (ostep * 1e-3) / 1e9, 2),
                 "tokens_per_s": round(o.batch / (ostep * 1e-3), 1),
-                "kernel": "MFMA decode" if o.num_q_heads // o.num_kv_heads >= 4 else "VALU decode"}
+                "kernel": "MFMA decode" if o.num_q_heads // o.num_kv_heads >= 3 else "VALU decode",
+                "kernel_us_events_mean": round(o_kms * 1000, 2),
+                "kernel_pct_hbm_peak": round(100 * okv / (o_kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
             del okc, ovc, oq, okn, ovn, osl, obt, octx, oout, ows, o
             torch.cuda.empty_cache()
 
@@ -460,6 +464,7 @@ def main():
                                        fscale, fscale, out, workspace=ws8)
 
         fstep, _, fev, _ = timed_loop(torch, nothing, append8, args.steps, args.warmup, flush)
+        f_kms = float(np.mean(kernel_times(torch, pa, append8, args.steps, flush)))
         kv8 = kv_bytes // 2
         # K/V codes instead of bf16; the new rows are read as bf16 and written as codes
         alg8 = alg - kv_bytes + kv8 - store_bytes(c) // 4
@@ -472,6 +477,8 @@ def main():
             "achieved_gb_s": round(alg8 / (fstep * 1e-3) / 1e9, 2),
             "frac_hbm_peak": round(alg8 / (fstep * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "algorithmic_bytes_per_launch": alg8,
+            "kernel_us_events_mean": round(f_kms * 1000, 2),
+            "kernel_frac_hbm_peak": round(alg8 / (f_kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "tokens_per_s": round(c.batch / (fstep * 1e-3), 1),
             "speedup_vs_bf16_step": round(ms_step / fstep, 3)}
         del k8, v8

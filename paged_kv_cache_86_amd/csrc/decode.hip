@@ -121,8 +121,22 @@ __device__ __forceinline__ void paged_decode_body(const DecodeArgs& a) {
   if (a.compact) {
     // Item bid / hg of the compacted list (its head groups on consecutive
     // workgroups, as in index order); workgroups past the last item exit.
-    const int item = bid / a.hg;
+    int item = bid / a.hg;
     hg = bid - item * a.hg;
+    if constexpr (KV8) {
+      // FP8 pools: inside each whole group of 8 items x hg head groups,
+      // workgroup r takes item r % 8 and head group r / 8.  Workgroups go to
+      // the 8 XCDs round-robin, so an XCD then serves every head group of its
+      // items instead of one head group of every item; with one head group per
+      // XCD, the XCD holding one of them ran 10-15% behind the others.
+      const int gsz = 8 * a.hg;
+      const int g = bid / gsz;
+      if ((g + 1) * gsz <= (int)gridDim.x) {
+        const int r = bid - g * gsz;
+        item = g * 8 + (r & 7);
+        hg = r >> 3;
+      }
+    }
     if (!decode_work_item<kCompactPerLane>(a, item, S, LONG, seq, split)) return;
   } else {
     hg = bid % a.hg;

@@ -695,12 +695,14 @@ __global__ __launch_bounds__(256) void paged_decode_combine_kernel(DecodeArgs a)
 // short split is 256 tokens at D = 128 and 512 tokens at D = 64.  A wave
 // keeps 4 chunks of loads in flight in a short split (all of them on FP8
 // pools; 4 instead of all 8 on bf16 pools measured level at 64 sequences and
-// 4% faster at 512) and one chunk in a long split.
+// 4% faster at 512); in a long split one chunk on bf16 pools and two on FP8
+// pools (FP8 headline step 1 us faster than with one; four: 2 us slower).
 constexpr bool kNontemporal = true;
 
 template <bool KV8> constexpr int tile_u() { return 2; }
 template <bool KV8> constexpr int tile_nit() { return KV8 ? 4 : 8; }
 template <bool KV8> constexpr int tile_depth() { return 4; }
+template <bool KV8> constexpr int tile_depth_long() { return KV8 ? 2 : 1; }
 template <bool KV8> constexpr int max_gt() { return KV8 ? 4 : 8; }
 
 template <int D, bool KV8>
@@ -714,7 +716,7 @@ template <int D, int GT, bool KV8, bool APPEND, bool LONG, bool SCALAR_BLK>
 void launch_main(const DecodeArgs& a, unsigned nwg, hipStream_t stream, hipEvent_t t_start,
                  hipEvent_t t_end) {
   hipExtLaunchKernelGGL((paged_decode_kernel<D, GT, tile_u<KV8>(), tile_nit<KV8>(),
-                                             tile_depth<KV8>(), tile_depth<KV8>() / 4, LONG,
+                                             tile_depth<KV8>(), tile_depth_long<KV8>(), LONG,
                                              kNontemporal, KV8, APPEND, SCALAR_BLK>),
                         dim3(nwg), dim3(256), 0, stream, t_start, t_end, 0u, a);
 }

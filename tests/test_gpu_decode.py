@@ -294,8 +294,10 @@ def _mfma_long_case(seed, D, BS, B=128):
 @pytest.mark.parametrize("D,BS", [(128, 16), (64, 1), (128, 1024)])
 def test_decode_mfma_long_splits(D, BS):
     """The MFMA kernel's 2,048-token splits (one chunk of loads in flight per wave, the block
-    ids of a split staged in LDS — 2,048 of them at block size 1 — or a split over two blocks):
-    every sequence against the oracle, plain and fused store."""
+    ids of a split staged in LDS — 2,048 of them at block size 1 — or a split over two
+    blocks): every sequence against the oracle, plain and fused store, and
+    the same outputs bit for bit from a NaN-filled workspace (every partial the merge reads was
+    written by this call)."""
     dev = device()
     c = _mfma_long_case(5151 + D + BS, D, BS)
     B = c.batch
@@ -313,6 +315,8 @@ def test_decode_mfma_long_splits(D, BS):
     say(f"[decode-mfma-long] D={D} BS={BS}: max|err| {err:.3e}")
     assert err <= ATOL
     assert np.all(out32[list(c.context_lens).index(0)] == 0)
+    nan_ws = torch.full((ws[2],), 0xFF, dtype=torch.uint8, device=dev)
+    assert np.array_equal(as_f64(d.decode(torch.float32, workspace=nan_ws)), out32)
     check_append(c, dev, f"mfma long splits D{D} BS{BS}", ref=ref)
 
 

@@ -102,7 +102,7 @@ __device__ __forceinline__ float shfl_xor(float v, int mask) {
 // Compacted decode work list.  The (sequence, split) items of a decode call,
 // sequences in order and each sequence's splits in order, where a sequence of
 // context ctx (clamped to [0, cap]) has max(1, ceil(ctx / S)) splits, or
-// ceil(ctx / 2S) when long splits are on and it needs more than nsplit_max
+// ceil(ctx / 2S) when long splits are on and it needs more than long_above
 // short ones.  Finds item `item` for the calling wave: lane l counts the
 // splits of sequences l*k .. l*k+k-1 (k = ceil(B / 64) <= PER_LANE), a wave
 // scan turns the counts into each lane's first item, and the lane holding
@@ -127,7 +127,7 @@ __device__ __forceinline__ bool decode_work_item(const Args& a, int item, int S,
     if (j < k && s0 + j < B) {
       const int ctx = ctxs[j] < 0 ? 0 : (ctxs[j] > cap ? cap : ctxs[j]);
       const int nshort = ctx == 0 ? 1 : (ctx + S - 1) / S;
-      n = (long_ok && nshort > a.nsplit_max) ? (ctx + 2 * S - 1) / (2 * S) : nshort;
+      n = (long_ok && nshort > a.long_above) ? (ctx + 2 * S - 1) / (2 * S) : nshort;
     }
     cnt[j] = n;
     tot += n;

@@ -56,7 +56,8 @@ __device__ __forceinline__ uint32_t pack_bf16_pair(float lo, float hi) {
 //
 // Splits.  A short split is S = kWaves * NIT chunks of U * RPW tokens (wave w
 // takes chunks w, w + 4, ...).  With LONG, a context needing more than
-// nsplit_max short splits is cut into long splits of 2S tokens instead, so
+// long_above short splits (nsplit_max, or 1 on FP8 pools) is cut into long
+// splits of 2S tokens instead (at most nsplit_max of them), so
 // one grid of nsplit_max workgroups per (sequence, head group) serves every
 // context the table allows: short contexts leave fewer workgroups idle, long
 // ones run fewer, longer workgroups (their per-workgroup set-up and merge are
@@ -209,7 +210,7 @@ __device__ __forceinline__ void paged_decode_body(const DecodeArgs& a) {
   const int cap = a.mbs << a.bs_log2;
   ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
   const int nshort = ctx == 0 ? 1 : (ctx + S - 1) / S;
-  const bool lng = LONG && nshort > a.nsplit_max;
+  const bool lng = LONG && nshort > a.long_above;
   const int nsplit = lng ? (ctx + SL - 1) / SL : nshort;
 
   // APPEND: lanes 0 .. 2*NLB-1 of wave 0 write the new row (bf16, or E4M3
@@ -632,7 +633,7 @@ __global__ __launch_bounds__(256) void paged_decode_combine_kernel(DecodeArgs a)
   const int cap = a.mbs << a.bs_log2;
   ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
   int nsplit = (ctx + S - 1) / S;
-  if (a.long_splits && nsplit > a.nsplit_max) nsplit = (ctx + 2 * S - 1) / (2 * S);
+  if (a.long_splits && nsplit > a.long_above) nsplit = (ctx + 2 * S - 1) / (2 * S);
   if (nsplit <= 1) return;  // written directly by the main kernel
   const int kvh = hg / a.nsub;
   const int sub = hg - kvh * a.nsub;
@@ -851,6 +852,11 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int head_dim, int block_size, int
   p.long_splits = !p.mfma && block_size >= S && p.nsplit_short >= kLongSplitMinShort &&
                   units * half >= (kv8 ? kLongSplitMinGridFp8 : kLongSplitMinGrid);
   p.nsplit_max = p.long_splits ? (int)half : p.nsplit_short;
+  // FP8 pools take long splits for every context of more than one short
+  // split (fewer, longer items: the FP8 headline step 1 us faster); bf16
+  // pools only for contexts that do not fit the halved slots (for all of
+  // them, the 512-sequence decode was 414-419 against 361-364 us).
+  p.long_above = kv8 ? 1 : p.nsplit_max;
   p.compact = B <= kCompactMaxSeqs;
   const int64_t parts = units * p.nsplit_max * p.gt;
   auto round256 = [](size_t x) { return (x + 255) / 256 * 256; };

@@ -57,7 +57,8 @@ struct DecodePlan {
   int gt;          // query heads handled by one workgroup (<= 8)
   int split_log2;    // tokens per short split = 1 << split_log2
   int nsplit_short;  // short splits of the longest possible context
-  bool long_splits;  // contexts above nsplit_max short splits use splits of twice the length
+  bool long_splits;  // contexts above long_above short splits use splits of twice the length
+  int long_above;    // nsplit_max on bf16 pools, 1 on FP8 pools (with long_splits)
   int nsplit_max;    // workgroups (and partial slots) per (sequence, head group)
   bool mfma;         // the MFMA kernel (bf16 pools, large query-head groups)
   bool compact;      // workgroups take compacted (sequence, split) items
@@ -85,6 +86,7 @@ struct DecodeArgs {
   float* ws_o;
   int mbs, Hq, Hkv, group, nsub, hg, bs_log2, split_log2, nsplit_max, num_blocks, out_f32;
   int long_splits;    // see DecodePlan
+  int long_above;     // see DecodePlan
   int batch;          // sequences (B)
   int compact;        // see DecodePlan
   float scale_log2e;  // softmax scale (times the K scale of an FP8 cache) times log2(e)

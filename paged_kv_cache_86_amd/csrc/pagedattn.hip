@@ -170,6 +170,7 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   a.split_log2 = p.split_log2;
   a.nsplit_max = p.nsplit_max;
   a.long_splits = p.long_splits;
+  a.long_above = p.long_above;
   a.batch = num_seqs;
   a.compact = p.compact;
   a.num_blocks = num_blocks;

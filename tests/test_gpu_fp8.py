@@ -272,12 +272,13 @@ def test_decode_append_fp8(case):
 
 
 def test_decode_fp8_long_splits():
-    """128 x 16/8 heads at block 256: contexts above 8 short splits take splits of 512 tokens
-    (both kinds and every boundary) on an FP8 pool, plain and fused store."""
+    """128 x 16/8 heads at block 256: on an FP8 pool every context of more than one short
+    split takes splits of 512 tokens (one-split contexts and every boundary around 1, 2, 8, 9
+    and 16 short splits), plain and fused store."""
     dev = device()
     S = 256
     edges = [1, 2, S - 1, S, S + 1, 8 * S - 1, 8 * S, 8 * S + 1, 9 * S, 9 * S + 1, 16 * S - 1,
-             16 * S, 0, 2 * S + 1]
+             16 * S, 0, 2 * S, 2 * S + 1, 3 * S - 1]
     rng = np.random.default_rng(4444)
     ctx = edges + [int(x) for x in rng.integers(1, 16 * S, 128 - len(edges), endpoint=True)]
     c = decode_case(4444, ctx, 16, 8, 128, 256, nb_factor=1.2, max_blocks_per_seq=16)

@@ -39,3 +39,10 @@ def test_traffic_record_follows_the_sources(tmp_path):
     src.write_bytes(b"kernel text, edited")
     assert bench.counter_traffic(str(rec)) is None
     assert bench.counter_traffic(str(tmp_path / "missing.json")) is None
+
+
+def test_committed_traffic_record_matches_the_current_sources():
+    """The committed counter record was taken from the decode sources as they stand, so the
+    bench line carries roofline.traffic (an edit of those sources needs new counter runs)."""
+    traffic = bench.counter_traffic(os.path.join(ROOT, "profiles", "paged_decode_traffic.json"))
+    assert traffic is not None and traffic > 0

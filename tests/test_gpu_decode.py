@@ -376,8 +376,9 @@ COMPACT_CASES = [(4, 2, 256), (14, 2, 16)]  # (Hq, Hkv, block size): VALU kernel
 @pytest.mark.parametrize("Hq,Hkv,BS", COMPACT_CASES, ids=[f"h{a}-{b}_bs{c}" for a, b, c in COMPACT_CASES])
 def test_decode_compact_list_matches_index_order(Hq, Hkv, BS):
     """Batches of up to 256 sequences take their splits from a compacted list, larger batches
-    in index order: 256 sequences, and the same 256 plus one padded row (257, index order),
-    give bit-identical outputs, plain and fused; the padded row is zero; both match the oracle."""
+    split-major (every sequence's first split, then every second split, ...): 256 sequences,
+    and the same 256 plus one padded row (257, split-major), give bit-identical outputs, plain
+    and fused; the padded row is zero; both match the oracle."""
     dev = device()
     rng = np.random.default_rng(5150 + Hq)
     ctx = [0, 1, 255, 256, 257, 2048] + [int(x) for x in rng.integers(0, 2048, 250, endpoint=True)]
@@ -424,10 +425,10 @@ REUSE_SHAPES = [  # (Hq, Hkv, D, BS, MBS, batch): VALU short / long splits, MFMA
 
 
 def test_decode_workspace_reuse_matches_fresh_workspace():
-    """The last workgroup of each (sequence, head group) merges the split partials, counting
-    arrivals in the workspace.  One workspace that starts as garbage and is reused by calls of
-    different shapes and data, back to back on the stream, gives bit-identical outputs to
-    calls on freshly zeroed workspaces (no stale partial or count is ever read)."""
+    """The split partials go to the workspace and a second kernel merges them.  One workspace
+    that starts as garbage and is reused by calls of different shapes and data, back to back on
+    the stream, gives bit-identical outputs to calls on freshly zeroed workspaces (no stale
+    partial is ever read)."""
     dev = device()
     rng = np.random.default_rng(4242)
     nbytes = max(pa.decode_workspace_bytes(B, Hq, Hkv, D, BS, MBS)

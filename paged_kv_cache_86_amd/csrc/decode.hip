@@ -25,8 +25,8 @@
 //     (the host does not know the lengths); for batches of up to 256
 //     sequences each workgroup looks its (sequence, split) up in the
 //     compacted list of the splits that exist, and larger batches take their
-//     slots split-major, so either way the empty slots end up at the end of
-//     the grid instead of between the real ones.  The
+//     slots split-major from the last slot down, so the empty slots do not
+//     sit between the real ones all through the grid.  The
 //     kernel boundary is what makes one XCD's partials visible to another:
 //     an in-kernel "last workgroup merges" scheme needs a device-scope
 //     release/acquire per workgroup, which on this chip writes back and
@@ -141,14 +141,18 @@ __device__ __forceinline__ void paged_decode_body(const DecodeArgs& a) {
     }
     if (!decode_work_item<kCompactPerLane>(a, item, S, LONG, seq, split)) return;
   } else {
-    // Split-major: every sequence's first split, then every second split, ...
-    // so the empty slots of short contexts gather at the end of the grid
-    // instead of taking workgroup slots from real work throughout (the
-    // 512-sequence decode: 361-364 -> 346-348 us).
+    // Split-major from the last split slot down: every sequence's last slot,
+    // then every second-to-last, ..., every first split at the end.  The
+    // empty slots of short contexts are then gone early, between the longest
+    // contexts' splits, instead of taking workgroup slots from real work all
+    // through the grid, and the grid ends on the dense first splits (the
+    // 512-sequence decode: 361-364 us in index order, 346-348 first split
+    // first, 336 last slot first).
     hg = bid % a.hg;
     const int rest = bid / a.hg;
-    split = rest / a.batch;
-    seq = rest - split * a.batch;
+    const int blk = rest / a.batch;
+    seq = rest - blk * a.batch;
+    split = a.nsplit_max - 1 - blk;
   }
   const int kvh = hg / a.nsub;
   const int sub = hg - kvh * a.nsub;

@@ -25,9 +25,9 @@ constexpr int64_t kLongSplitMinGrid = 8192;
 constexpr int64_t kLongSplitMinGridFp8 = 1024;
 // Decode grids of up to this many sequences take their (sequence, split)
 // items from a compacted list (4 sequences per lane of one wave in the
-// lookup); larger batches take their slots split-major (every sequence's
-// first split, then every second split, ...), where the lookup's extra round
-// trip costs more than the empty workgroups it removes (measured at 512).
+// lookup); larger batches take their slots split-major from the last slot
+// down, where the lookup's extra round trip costs more than the empty
+// workgroups it removes (measured at 512).
 constexpr int kCompactPerLane = 4;
 constexpr int kCompactMaxSeqs = 64 * kCompactPerLane;
 // Query heads per KV head from which decode runs on MFMA (bf16 and FP8

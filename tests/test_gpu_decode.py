@@ -376,9 +376,9 @@ COMPACT_CASES = [(4, 2, 256), (14, 2, 16)]  # (Hq, Hkv, block size): VALU kernel
 @pytest.mark.parametrize("Hq,Hkv,BS", COMPACT_CASES, ids=[f"h{a}-{b}_bs{c}" for a, b, c in COMPACT_CASES])
 def test_decode_compact_list_matches_index_order(Hq, Hkv, BS):
     """Batches of up to 256 sequences take their splits from a compacted list, larger batches
-    split-major (every sequence's first split, then every second split, ...): 256 sequences,
-    and the same 256 plus one padded row (257, split-major), give bit-identical outputs, plain
-    and fused; the padded row is zero; both match the oracle."""
+    split-major from the last split slot down: 256 sequences, and the same 256 plus one padded
+    row (257, split-major), give bit-identical outputs, plain and fused; the padded row is
+    zero; both match the oracle."""
     dev = device()
     rng = np.random.default_rng(5150 + Hq)
     ctx = [0, 1, 255, 256, 257, 2048] + [int(x) for x in rng.integers(0, 2048, 250, endpoint=True)]

@@ -320,6 +320,27 @@ def test_decode_mfma_long_splits(D, BS):
     check_append(c, dev, f"mfma long splits D{D} BS{BS}", ref=ref)
 
 
+def test_decode_mfma_long_splits_split_major():
+    """300 sequences (past the compacted list) with 2,048-token MFMA splits: the grid's slots
+    go split-major from the last slot down; every sequence against the oracle, plain and fused
+    store, and the same outputs from a NaN-filled workspace."""
+    dev = device()
+    c = _mfma_long_case(5353, 128, 16, B=300)
+    say(f"[decode-mfma-long] split-major B={c.batch} ctx max {int(c.context_lens.max())}")
+    d = DecodeOnDevice(c, dev)
+    d.store()
+    out32 = as_f64(d.decode(torch.float32))
+    kc, vc = oracle.kvcache_store(c.k_new, c.v_new, c.slot_mapping, c.k_cache, c.v_cache)
+    ref = oracle.paged_decode(c.q, kc, vc, c.block_tables, c.context_lens, np.float32(c.scale))
+    err = np.abs(out32 - ref).max()
+    say(f"[decode-mfma-long] split-major: max|err| {err:.3e}")
+    assert err <= ATOL
+    nan_ws = torch.full((pa.decode_workspace_bytes(c.batch, 28, 4, 128, 16, c.max_blocks_per_seq),),
+                        0xFF, dtype=torch.uint8, device=dev)
+    assert np.array_equal(as_f64(d.decode(torch.float32, workspace=nan_ws)), out32)
+    check_append(c, dev, "mfma long splits, split-major", ref=ref)
+
+
 MAX_CASES = [(128, 2), (128, 7), (64, 2), (64, 7)]  # VALU (2 heads per KV head) and MFMA (7)
 
 

@@ -101,6 +101,7 @@ SMALL = [
     (128, 16, 20, 1, [700, 1, 257]),           # 20 heads: two MFMA sub-groups of 10
     (64, 32, 32, 1, [64, 1000, 3]),            # 32 heads: two MFMA sub-groups of 16
     (128, 64, 3, 1, [1, 64, 65, 1000]),        # 3 heads: the smallest MFMA group
+    (128, 256, 16, 8, [3000]),                 # one sequence: its first split, then 11 more
     (128, 512, 3, 3, [1500, 2]),
     (128, 1024, 2, 2, [3000, 1025]),
 ]
